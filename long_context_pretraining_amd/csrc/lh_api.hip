@@ -1,0 +1,256 @@
+// C ABI of the Lighthouse Attention library (declared in include/lighthouse.h):
+// host-side validation and sizing, then asynchronous launches on the caller's
+// stream.  No allocation, no synchronisation, no state beyond the constant
+// kernel table.
+#include <math.h>
+#include <string.h>
+
+#include "lh_internal.h"
+
+namespace {
+
+constexpr size_t kAlign = 256;
+inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+inline int64_t round64(int64_t x) { return (x + 63) / 64 * 64; }
+inline size_t esize(int dtype) { return dtype == LH_BF16 ? 2 : 4; }
+
+bool aligned(const void* p) { return p && ((uintptr_t)p % 16) == 0; }
+
+lh_status plan_impl(const lh_desc* d, lh_plan* out, LhGeom* g) {
+    if (!d || !out) return LH_E_ARG;
+    if (d->B < 1 || d->H < 1 || d->N < 1 || d->d < 1 || d->p < 2 || d->L < 1 || d->L > LH_MAX_LEVELS || d->k < 1)
+        return LH_E_ARG;
+    if (d->dtype != LH_F32 && d->dtype != LH_BF16) return LH_E_ARG;
+    if (d->d % 8) return LH_E_ARG;
+    int64_t pw[LH_MAX_LEVELS];
+    pw[0] = 1;
+    for (int l = 1; l < d->L; ++l) {
+        if (pw[l - 1] > d->N / d->p) return LH_E_ARG;   // p^l would exceed N
+        pw[l] = pw[l - 1] * d->p;
+    }
+    if (d->N % pw[d->L - 1]) return LH_E_ARG;
+    if (d->dtype == LH_BF16 && d->d != 64 && d->d != 128) return LH_E_UNSUPPORTED;
+    if (d->dtype == LH_F32 && d->d != 64) return LH_E_UNSUPPORTED;
+
+    lh_plan P;
+    memset(&P, 0, sizeof(P));
+    LhGeom G;
+    memset(&G, 0, sizeof(G));
+    int64_t off = 0, S = 0, words = 0;
+    for (int l = 0; l < d->L; ++l) {
+        P.M[l] = d->N / pw[l];
+        P.level_off[l] = off;
+        off += P.M[l];
+        P.k_eff[l] = l ? (d->k < P.M[l] ? d->k : P.M[l]) : 0;
+        S += l ? d->p * P.k_eff[l] : 0;
+        G.words_off[l] = words;
+        if (l) words += (P.M[l] + 31) / 32;
+        G.pw[l] = pw[l];
+    }
+    P.level_off[d->L] = off;
+    G.words_off[d->L] = words;
+    P.M_total = off;
+    P.S = S + P.M[d->L - 1];
+    P.S_formula = d->N / pw[d->L - 1] + (int64_t)(d->L - 1) * d->p * d->k;
+    P.S_pad = round64(P.S);
+    if (P.M_total >= ((int64_t)1 << 31)) return LH_E_UNSUPPORTED;
+
+    const int64_t BH = d->B * d->H, Mu = P.M_total - d->N;
+    const size_t e = esize(d->dtype);
+    const size_t row = (size_t)BH * P.S * d->d * e;          // [BH,S,d] dtype
+    const size_t colT = (size_t)BH * d->d * P.S_pad * e;     // [BH,d,S_pad] dtype
+    const size_t rowf = (size_t)BH * P.S * d->d * 4;         // [BH,S,d] f32
+    const size_t vec = (size_t)BH * P.S * 4;                 // [BH,S] f32
+
+    P.pyr_bytes = (size_t)3 * BH * Mu * d->d * e;
+    P.sel_ws_bytes = align_up((size_t)BH * Mu * 4) + 2 * align_up((size_t)BH * words * 4);
+    size_t o = 0;
+    const size_t fwd_sizes[8] = {row, row, row, colT, colT, colT, rowf, vec};
+    for (int i = 0; i < 8; ++i) { P.fwd_off[i] = o; o += align_up(fwd_sizes[i]); }
+    P.fwd_ws_bytes = o;
+    o = 0;
+    const size_t bwd_sizes[6] = {row, colT, vec, rowf, rowf, rowf};
+    for (int i = 0; i < 6; ++i) { P.bwd_off[i] = o; o += align_up(bwd_sizes[i]); }
+    P.bwd_ws_bytes = o;
+    const int64_t N_pad = round64(d->N);
+    const size_t dT = (size_t)BH * d->d * N_pad * e;
+    P.dense_fwd_ws_bytes = align_up(dT) + align_up((size_t)BH * d->N * d->d * 4);
+    P.dense_bwd_ws_bytes = 3 * align_up(dT) + align_up((size_t)BH * d->N * 4);
+
+    *out = P;
+    if (g) {
+        G.BH = BH; G.N = d->N; G.d = d->d; G.S = P.S; G.S_pad = P.S_pad; G.M_total = P.M_total; G.Mu = Mu;
+        G.p = d->p; G.L = d->L;
+        for (int l = 0; l < d->L; ++l) { G.M[l] = P.M[l]; G.k_eff[l] = P.k_eff[l]; }
+        for (int l = 0; l <= d->L; ++l) G.off[l] = P.level_off[l];
+        G.words_total = words;
+        *g = G;
+    }
+    return LH_OK;
+}
+
+inline lh_status dev(hipError_t e) { return e == hipSuccess ? LH_OK : LH_E_DEVICE; }
+inline unsigned char* at(void* base, size_t off) { return static_cast<unsigned char*>(base) + off; }
+inline const unsigned char* at(const void* base, size_t off) { return static_cast<const unsigned char*>(base) + off; }
+
+float softmax_scale(const lh_desc* d) { return d->scale > 0.f ? d->scale : 1.0f / sqrtf((float)d->d); }
+
+}  // namespace
+
+extern "C" {
+
+lh_status lh_make_plan(const lh_desc* desc, lh_plan* out) { return plan_impl(desc, out, nullptr); }
+
+const char* lh_status_string(int s) {
+    switch (s) {
+        case LH_OK: return "ok";
+        case LH_E_ARG: return "invalid argument (pointer, shape or parameter)";
+        case LH_E_UNSUPPORTED: return "unsupported configuration (dtype/d/size not built)";
+        case LH_E_WORKSPACE: return "workspace smaller than lh_make_plan reports";
+        case LH_E_DEVICE: return "HIP launch failed";
+        default: return "unknown status";
+    }
+}
+
+lh_status lh_pyramid(const lh_desc* desc, const void* q, const void* k, const void* v, void* pyr, size_t pyr_bytes,
+                     void* stream) {
+    lh_plan P;
+    LhGeom g;
+    lh_status s = plan_impl(desc, &P, &g);
+    if (s != LH_OK) return s;
+    if (!aligned(q) || !aligned(k) || !aligned(v)) return LH_E_ARG;
+    if (P.pyr_bytes == 0) return LH_OK;
+    if (!aligned(pyr)) return LH_E_ARG;
+    if (pyr_bytes < P.pyr_bytes) return LH_E_WORKSPACE;
+    return dev(launch_pool(g, desc->dtype, q, k, v, pyr, (hipStream_t)stream));
+}
+
+lh_status lh_score_topk(const lh_desc* desc, const void* q, const void* k, int32_t* gidx, int32_t* gpos, void* ws,
+                        size_t ws_bytes, void* stream) {
+    lh_plan P;
+    LhGeom g;
+    lh_status s = plan_impl(desc, &P, &g);
+    if (s != LH_OK) return s;
+    if (!aligned(q) || !aligned(k) || !aligned(gidx) || !aligned(gpos)) return LH_E_ARG;
+    if (P.sel_ws_bytes && !aligned(ws)) return LH_E_ARG;
+    if (ws_bytes < P.sel_ws_bytes) return LH_E_WORKSPACE;
+    hipStream_t st = (hipStream_t)stream;
+    float* sigma = (float*)ws;
+    const size_t sz_sigma = align_up((size_t)g.BH * g.Mu * 4), sz_w = align_up((size_t)g.BH * g.words_total * 4);
+    uint32_t* words = (uint32_t*)at(ws, sz_sigma);
+    int32_t* prefix = (int32_t*)at(ws, sz_sigma + sz_w);
+    hipError_t e = launch_scores(g, desc->dtype, q, k, sigma, st);
+    if (e == hipSuccess) e = launch_topk(g, sigma, words, prefix, st);
+    if (e == hipSuccess) e = launch_map(g, words, prefix, gidx, gpos, st);
+    return dev(e);
+}
+
+lh_status lh_forward(const lh_desc* desc, const void* q, const void* k, const void* v, const void* pyr,
+                     const int32_t* gidx, const int32_t* gpos, void* o, void* fwd_ws, size_t fwd_ws_bytes,
+                     void* stream) {
+    lh_plan P;
+    LhGeom g;
+    lh_status s = plan_impl(desc, &P, &g);
+    if (s != LH_OK) return s;
+    if (!aligned(q) || !aligned(k) || !aligned(v) || !aligned(gidx) || !aligned(gpos) || !aligned(o) ||
+        !aligned(fwd_ws))
+        return LH_E_ARG;
+    if (P.pyr_bytes && !aligned(pyr)) return LH_E_ARG;
+    if (fwd_ws_bytes < P.fwd_ws_bytes) return LH_E_WORKSPACE;
+    hipStream_t st = (hipStream_t)stream;
+    void* rows[3] = {at(fwd_ws, P.fwd_off[LH_FWD_QG]), at(fwd_ws, P.fwd_off[LH_FWD_KG]), at(fwd_ws, P.fwd_off[LH_FWD_VG])};
+    void* cols[3] = {at(fwd_ws, P.fwd_off[LH_FWD_QT]), at(fwd_ws, P.fwd_off[LH_FWD_KT]), at(fwd_ws, P.fwd_off[LH_FWD_VT])};
+    float* og = (float*)at(fwd_ws, P.fwd_off[LH_FWD_O]);
+    float* lse = (float*)at(fwd_ws, P.fwd_off[LH_FWD_LSE]);
+    hipError_t e = launch_gather(g, desc->dtype, q, k, v, pyr, gidx, rows, cols, st);
+    if (e == hipSuccess) {
+        AttnArgs a{g.BH, g.S, g.S_pad, g.d, softmax_scale(desc)};
+        e = launch_attn_fwd(a, desc->dtype, rows[0], rows[1], cols[2], og, nullptr, lse, st);
+    }
+    if (e == hipSuccess) e = launch_scatter_fwd(g, desc->dtype, og, gpos, o, st);
+    return dev(e);
+}
+
+lh_status lh_backward(const lh_desc* desc, const int32_t* gidx, const int32_t* gpos, const void* fwd_ws,
+                      const void* dout, void* dq, void* dk, void* dv, void* bwd_ws, size_t bwd_ws_bytes,
+                      void* stream) {
+    lh_plan P;
+    LhGeom g;
+    lh_status s = plan_impl(desc, &P, &g);
+    if (s != LH_OK) return s;
+    if (!aligned(gidx) || !aligned(gpos) || !aligned(fwd_ws) || !aligned(dout) || !aligned(dq) || !aligned(dk) ||
+        !aligned(dv) || !aligned(bwd_ws))
+        return LH_E_ARG;
+    if (bwd_ws_bytes < P.bwd_ws_bytes) return LH_E_WORKSPACE;
+    hipStream_t st = (hipStream_t)stream;
+    const float* og = (const float*)at(fwd_ws, P.fwd_off[LH_FWD_O]);
+    const float* lse = (const float*)at(fwd_ws, P.fwd_off[LH_FWD_LSE]);
+    void* dog = at(bwd_ws, P.bwd_off[LH_BWD_DO]);
+    void* dogT = at(bwd_ws, P.bwd_off[LH_BWD_DOT]);
+    float* Dv = (float*)at(bwd_ws, P.bwd_off[LH_BWD_D]);
+    float* dxg[3] = {(float*)at(bwd_ws, P.bwd_off[LH_BWD_DQ]), (float*)at(bwd_ws, P.bwd_off[LH_BWD_DK]),
+                     (float*)at(bwd_ws, P.bwd_off[LH_BWD_DV])};
+    hipError_t e = launch_scatter_bwd(g, desc->dtype, dout, og, gidx, dog, dogT, Dv, st);
+    if (e == hipSuccess) {
+        AttnArgs a{g.BH, g.S, g.S_pad, g.d, softmax_scale(desc)};
+        e = launch_attn_bwd(a, desc->dtype, true, at(fwd_ws, P.fwd_off[LH_FWD_QG]), at(fwd_ws, P.fwd_off[LH_FWD_KG]),
+                            at(fwd_ws, P.fwd_off[LH_FWD_VG]), at(fwd_ws, P.fwd_off[LH_FWD_QT]),
+                            at(fwd_ws, P.fwd_off[LH_FWD_KT]), dog, dogT, lse, Dv, dxg[0], dxg[1], dxg[2], st);
+    }
+    if (e == hipSuccess) {
+        const float* cg[3] = {dxg[0], dxg[1], dxg[2]};
+        void* outs[3] = {dq, dk, dv};
+        e = launch_gather_pool_bwd(g, desc->dtype, cg, gpos, outs, st);
+    }
+    return dev(e);
+}
+
+lh_status dense_causal_attn(const lh_desc* desc, const void* q, const void* k, const void* v, void* o, float* lse,
+                            void* ws, size_t ws_bytes, void* stream) {
+    lh_plan P;
+    lh_status s = plan_impl(desc, &P, nullptr);
+    if (s != LH_OK) return s;
+    if (!aligned(q) || !aligned(k) || !aligned(v) || !aligned(o) || !aligned(lse) || !aligned(ws)) return LH_E_ARG;
+    if (ws_bytes < P.dense_fwd_ws_bytes) return LH_E_WORKSPACE;
+    hipStream_t st = (hipStream_t)stream;
+    const int64_t BH = desc->B * desc->H, N = desc->N, N_pad = round64(N);
+    const size_t dT = align_up((size_t)BH * desc->d * N_pad * esize(desc->dtype));
+    float* o32 = (float*)at(ws, dT);
+    hipError_t e = launch_transpose(desc->dtype, BH, N, N_pad, desc->d, v, ws, st);
+    if (e == hipSuccess) {
+        AttnArgs a{BH, N, N_pad, desc->d, softmax_scale(desc)};
+        e = launch_attn_fwd(a, desc->dtype, q, k, ws, o32, o, lse, st);
+    }
+    return dev(e);
+}
+
+lh_status dense_causal_attn_backward(const lh_desc* desc, const void* q, const void* k, const void* v,
+                                     const float* lse, const void* fwd_ws, const void* dout, void* dq, void* dk,
+                                     void* dv, void* ws, size_t ws_bytes, void* stream) {
+    lh_plan P;
+    lh_status s = plan_impl(desc, &P, nullptr);
+    if (s != LH_OK) return s;
+    if (!aligned(q) || !aligned(k) || !aligned(v) || !aligned(fwd_ws) || !aligned(lse) || !aligned(dout) ||
+        !aligned(dq) || !aligned(dk) || !aligned(dv) || !aligned(ws))
+        return LH_E_ARG;
+    if (ws_bytes < P.dense_bwd_ws_bytes) return LH_E_WORKSPACE;
+    hipStream_t st = (hipStream_t)stream;
+    const int64_t BH = desc->B * desc->H, N = desc->N, N_pad = round64(N);
+    const size_t dT = align_up((size_t)BH * desc->d * N_pad * esize(desc->dtype));
+    void* qT = ws;
+    void* kT = at(ws, dT);
+    void* doT = at(ws, 2 * dT);
+    float* Dv = (float*)at(ws, 3 * dT);
+    const float* o32 = (const float*)at(fwd_ws, dT);
+    hipError_t e = launch_transpose(desc->dtype, BH, N, N_pad, desc->d, q, qT, st);
+    if (e == hipSuccess) e = launch_transpose(desc->dtype, BH, N, N_pad, desc->d, k, kT, st);
+    if (e == hipSuccess) e = launch_dense_bwd_prep(desc->dtype, BH, N, N_pad, desc->d, dout, o32, doT, Dv, st);
+    if (e == hipSuccess) {
+        AttnArgs a{BH, N, N_pad, desc->d, softmax_scale(desc)};
+        e = launch_attn_bwd(a, desc->dtype, desc->dtype == LH_F32, q, k, v, qT, kT, dout, doT, lse, Dv, dq, dk, dv,
+                            st);
+    }
+    return dev(e);
+}
+
+}  // extern "C"

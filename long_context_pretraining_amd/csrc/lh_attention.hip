@@ -1,0 +1,682 @@
+// Causal softmax attention on the gathered sub-sequence (page "skillsmp.com
+// ... lighthouse-attention", Stage 3: dense attention with the standard S x S
+// causal mask; gist.science Methodology 2C), forward and backward, on the
+// gfx950 matrix cores.  This is the only dense contraction of the layer.
+//
+// Design (wave64, v_mfma_f32_32x32x16_bf16; f32 uses v_mfma_f32_32x32x2_f32):
+//  * Forward and dQ compute the TRANSPOSED score tile S^T = K Q^T, so each lane
+//    owns one query column: the softmax row statistics are per-lane scalars
+//    plus one exchange with the lane 32 away.  P^T is then fed straight back
+//    as the B operand of O^T += V^T P^T (see the k-order note in lh_device.h),
+//    with V^T read from a transposed copy made by the gather.
+//  * dK/dV computes S = Q K^T (each lane owns one key column) and accumulates
+//    dV^T += dO^T P and dK^T += Q^T dS, again without moving P or dS across
+//    lanes.  dQ is a separate pass over key tiles (recomputing P), so every
+//    output is written exactly once: deterministic, no atomics.
+//  * K/V (or Q/dO) tiles are staged through LDS, double buffered with a
+//    register prefetch of the next tile; rows padded against bank conflicts.
+//  * Blocks are ordered longest-first (causal work grows with the block
+//    index), heads interleaved.
+#include <math.h>
+
+#include "lh_device.h"
+#include "lh_internal.h"
+
+namespace {
+
+constexpr int kThreads = 256;   // 4 waves
+constexpr int kBN = 64;         // keys (fwd, dQ) or queries (dK/dV) per LDS tile
+constexpr int kWaveRows = 64;   // queries (fwd, dQ) or keys (dK/dV) per wave
+constexpr int kBlockRows = 4 * kWaveRows;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+struct AttnK {
+    int64_t BH, S, S_pad;
+    float scale, scale_log2;
+    int nblk;   // row blocks per head
+};
+
+template <typename T> struct Pad { enum { ROW = 16 / (int)sizeof(T), COLT = 4 }; };
+
+// Cooperative copy of a [64 x D] row-major tile (rows r0.., bounds-checked
+// against S) into LDS (stride D + pad) through registers.
+template <typename T, int D>
+struct RowTile {
+    typedef typename Frag<T>::type F;
+    static constexpr int LD = D + Pad<T>::ROW;
+    static constexpr int UNITS = kBN * D / 8 / kThreads;   // 8-element units per thread
+    F r[UNITS];
+    __device__ __forceinline__ void load(const T* base, int64_t r0, int64_t S) {
+#pragma unroll
+        for (int u = 0; u < UNITS; ++u) {
+            const int id = threadIdx.x + u * kThreads;
+            const int row = id / (D / 8), col = (id % (D / 8)) * 8;
+            r[u] = load8_or_zero(base + (r0 + row) * D + col, r0 + row < S);
+        }
+    }
+    __device__ __forceinline__ void store(T* lds) const {
+#pragma unroll
+        for (int u = 0; u < UNITS; ++u) {
+            const int id = threadIdx.x + u * kThreads;
+            const int row = id / (D / 8), col = (id % (D / 8)) * 8;
+            *reinterpret_cast<F*>(lds + row * LD + col) = r[u];
+        }
+    }
+};
+
+// Cooperative copy of a [D x 64] slice (columns c0.. of a transposed array
+// with row length S_pad; always in bounds) into LDS (stride 64 + 4).
+template <typename T, int D>
+struct ColTile {
+    typedef typename Frag<T>::type F;
+    typedef typename Frag<T>::half Hf;
+    static constexpr int LD = kBN + Pad<T>::COLT;
+    static constexpr int UNITS = kBN * D / 8 / kThreads;
+    F r[UNITS];
+    __device__ __forceinline__ void load(const T* base, int64_t c0, int64_t S_pad) {
+#pragma unroll
+        for (int u = 0; u < UNITS; ++u) {
+            const int id = threadIdx.x + u * kThreads;
+            const int row = id / (kBN / 8), col = (id % (kBN / 8)) * 8;
+            r[u] = load8(base + row * S_pad + c0 + col);
+        }
+    }
+    __device__ __forceinline__ void store(T* lds) const {
+#pragma unroll
+        for (int u = 0; u < UNITS; ++u) {
+            const int id = threadIdx.x + u * kThreads;
+            const int row = id / (kBN / 8), col = (id % (kBN / 8)) * 8;
+            *reinterpret_cast<Hf*>(lds + row * LD + col) = r[u].lo;
+            *reinterpret_cast<Hf*>(lds + row * LD + col + 4) = r[u].hi;
+        }
+    }
+};
+
+__device__ __forceinline__ void block_order(const AttnK& a, bool longest_last_rows, int64_t& bh, int& blk) {
+    const int64_t x = blockIdx.x;
+    bh = x % a.BH;
+    const int i = (int)(x / a.BH);
+    blk = longest_last_rows ? (a.nblk - 1 - i) : i;
+}
+
+// The bf16 forward multiplies V by P in two parts, P = hi + lo with hi the
+// bf16 rounding of P and lo the bf16 rounding of the remainder, so that the
+// f32 output carries P to about 2^-17 relative.  Without it the output would
+// use P rounded to 8 bits while the backward recomputes P in f32, and
+// D = rowsum(dO * O) would then be off by ~2^-9 |dP| in rows dominated by a
+// few keys -- an error the products with K and Q magnify.
+template <typename T> constexpr bool kSplitP = sizeof(T) == 2;
+
+template <typename T>
+__device__ __forceinline__ void split_frag(const floatx16& c, int cc, typename Frag<T>::type& hi,
+                                          typename Frag<T>::type& lo) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const float x = c[8 * cc + e];
+        hi[e] = static_cast<T>(x);
+        if (kSplitP<T>) lo[e] = static_cast<T>(x - static_cast<float>(hi[e]));
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Forward: O = softmax(scale Q K^T, causal) V and LSE, per 256-query block.
+// The output is written in f32 (and, when Ot is given, also in T).
+// ---------------------------------------------------------------------------
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K,
+                                                            const T* __restrict__ VT, float* __restrict__ O32,
+                                                            T* __restrict__ Ot, float* __restrict__ LSE, AttnK a) {
+    typedef typename Frag<T>::type F;
+    typedef RowTile<T, D> KTile;
+    typedef ColTile<T, D> VTile;
+    constexpr int KSZ = kBN * KTile::LD, VSZ = D * VTile::LD;
+    extern __shared__ __align__(16) unsigned char smem[];
+    T* lds = reinterpret_cast<T*>(smem);
+
+    int64_t bh; int qb;
+    block_order(a, true, bh, qb);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int col = lane & 31, h = lane >> 5;
+    const int64_t S = a.S;
+    const T* Qh = Q + bh * S * D;
+    const T* Kh = K + bh * S * D;
+    const T* VTh = VT + bh * D * a.S_pad;
+
+    const int64_t q_blk0 = (int64_t)qb * kBlockRows;
+    const int64_t q_base = q_blk0 + wave * kWaveRows;
+    const int64_t q_last_blk = (q_blk0 + kBlockRows < S ? q_blk0 + kBlockRows : S) - 1;
+    const int64_t q_last_w = (q_base + kWaveRows < S ? q_base + kWaveRows : S) - 1;
+    const int ntiles = (int)(q_last_blk / kBN) + 1;
+
+    F qf[2][D / 16];
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+        const int64_t q = q_base + 32 * cb + col;
+#pragma unroll
+        for (int c = 0; c < D / 16; ++c) qf[cb][c] = load8_or_zero(Qh + q * D + 16 * c + 8 * h, q < S);
+    }
+    floatx16 o[2][D / 32];
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) o[cb][db] = floatx16{};
+    float m_i[2] = {-INFINITY, -INFINITY}, l_i[2] = {0.f, 0.f};
+
+    KTile kt_r;
+    VTile vt_r;
+    kt_r.load(Kh, 0, S);
+    vt_r.load(VTh, 0, a.S_pad);
+    kt_r.store(lds);
+    vt_r.store(lds + KSZ);
+    __syncthreads();
+
+    for (int t = 0; t < ntiles; ++t) {
+        const int buf = t & 1;
+        if (t + 1 < ntiles) {
+            kt_r.load(Kh, (int64_t)(t + 1) * kBN, S);
+            vt_r.load(VTh, (int64_t)(t + 1) * kBN, a.S_pad);
+        }
+        const T* lk = lds + buf * (KSZ + VSZ);
+        const T* lv = lk + KSZ;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            const int64_t kbase = (int64_t)t * kBN + 32 * ks;
+            if (kbase > q_last_w) continue;
+            floatx16 s[2] = {floatx16{}, floatx16{}};
+#pragma unroll
+            for (int c = 0; c < D / 16; ++c) {
+                const F kf = load8(lk + (32 * ks + col) * KTile::LD + 16 * c + 8 * h);
+                mma_k16(s[0], kf, qf[0][c]);
+                mma_k16(s[1], kf, qf[1][c]);
+            }
+            const bool need_mask = (kbase + 31 > q_base) || (kbase + 31 >= S);
+#pragma unroll
+            for (int cb = 0; cb < 2; ++cb) {
+                const int64_t q = q_base + 32 * cb + col;
+                float mx = -INFINITY;
+#pragma unroll
+                for (int j = 0; j < 16; ++j) {
+                    float v = s[cb][j] * a.scale_log2;
+                    if (need_mask) {
+                        const int64_t key = kbase + c_row(j, h);
+                        if (key > q || key >= S) v = -INFINITY;
+                    }
+                    s[cb][j] = v;
+                    mx = fmaxf(mx, v);
+                }
+                mx = fmaxf(mx, xor32(mx));
+                const float m_new = fmaxf(m_i[cb], mx);
+                const float m_use = m_new == -INFINITY ? 0.f : m_new;
+                const float alpha = fast_exp2(m_i[cb] - m_use);
+                float rs = 0.f;
+#pragma unroll
+                for (int j = 0; j < 16; ++j) {
+                    const float p = fast_exp2(s[cb][j] - m_use);
+                    s[cb][j] = p;
+                    rs += p;
+                }
+                l_i[cb] = l_i[cb] * alpha + rs;
+                m_i[cb] = m_new;
+#pragma unroll
+                for (int db = 0; db < D / 32; ++db) o[cb][db] *= alpha;
+            }
+#pragma unroll
+            for (int c2 = 0; c2 < 2; ++c2) {
+                F p0, p1, r0, r1;
+                split_frag<T>(s[0], c2, p0, r0);
+                split_frag<T>(s[1], c2, p1, r1);
+#pragma unroll
+                for (int db = 0; db < D / 32; ++db) {
+                    const F vf = load_4_4(lv + (32 * db + col) * VTile::LD + 32 * ks + 16 * c2 + 4 * h);
+                    mma_k16(o[0][db], vf, p0);
+                    mma_k16(o[1][db], vf, p1);
+                    if (kSplitP<T>) {
+                        mma_k16(o[0][db], vf, r0);
+                        mma_k16(o[1][db], vf, r1);
+                    }
+                }
+            }
+        }
+        if (t + 1 < ntiles) {
+            T* nb = lds + (buf ^ 1) * (KSZ + VSZ);
+            kt_r.store(nb);
+            vt_r.store(nb + KSZ);
+        }
+        __syncthreads();
+    }
+
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+        const int64_t q = q_base + 32 * cb + col;
+        const float l = l_i[cb] + xor32(l_i[cb]);
+        const float inv = 1.f / l;
+        if (q < S) {
+            float* orow = O32 + (bh * S + q) * D;
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    floatx4 w;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) w[i] = o[cb][db][4 * m + i] * inv;
+                    *reinterpret_cast<floatx4*>(orow + 32 * db + 8 * m + 4 * h) = w;
+                    if (Ot) {
+                        typename Frag<T>::half wt;
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) wt[i] = static_cast<T>(w[i]);
+                        *reinterpret_cast<typename Frag<T>::half*>(Ot + (bh * S + q) * D + 32 * db + 8 * m + 4 * h) = wt;
+                    }
+                }
+            if (h == 0) LSE[bh * S + q] = (m_i[cb] + log2f(l)) * kLn2;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// dQ: per 256-query block, over key tiles: S^T = K Q^T, P^T, dP^T = V dO^T,
+// dS^T = P^T (dP^T - D), dQ^T += K^T dS^T.
+// Each row of dS sums to zero, so dQ = scale sum_j dS_j K_j is a cancelling
+// sum; with dS rounded to 8 bits the remainder would carry 2^-9 |dS| |K| of
+// noise.  bf16 therefore feeds dS as hi + lo parts (as P in the forward).
+// ---------------------------------------------------------------------------
+template <typename T, int D, typename OutT>
+__global__ __launch_bounds__(kThreads) void attn_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K,
+                                                           const T* __restrict__ V, const T* __restrict__ KT,
+                                                           const T* __restrict__ dO, const float* __restrict__ LSE,
+                                                           const float* __restrict__ Dv, OutT* __restrict__ dQ,
+                                                           AttnK a) {
+    typedef typename Frag<T>::type F;
+    typedef RowTile<T, D> RT;
+    typedef ColTile<T, D> CT;
+    constexpr int RSZ = kBN * RT::LD, CSZ = D * CT::LD, BUF = 2 * RSZ + CSZ;
+    extern __shared__ __align__(16) unsigned char smem[];
+    T* lds = reinterpret_cast<T*>(smem);
+
+    int64_t bh; int qb;
+    block_order(a, true, bh, qb);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int col = lane & 31, h = lane >> 5;
+    const int64_t S = a.S;
+    const T* Qh = Q + bh * S * D;
+    const T* Kh = K + bh * S * D;
+    const T* Vh = V + bh * S * D;
+    const T* KTh = KT + bh * D * a.S_pad;
+    const T* dOh = dO + bh * S * D;
+
+    const int64_t q_blk0 = (int64_t)qb * kBlockRows;
+    const int64_t q_base = q_blk0 + wave * kWaveRows;
+    const int64_t q_last_blk = (q_blk0 + kBlockRows < S ? q_blk0 + kBlockRows : S) - 1;
+    const int64_t q_last_w = (q_base + kWaveRows < S ? q_base + kWaveRows : S) - 1;
+    const int ntiles = (int)(q_last_blk / kBN) + 1;
+
+    F qf[2][D / 16], df[2][D / 16];
+    float lse2[2], dd[2];
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+        const int64_t q = q_base + 32 * cb + col;
+        const bool ok = q < S;
+#pragma unroll
+        for (int c = 0; c < D / 16; ++c) {
+            qf[cb][c] = load8_or_zero(Qh + q * D + 16 * c + 8 * h, ok);
+            df[cb][c] = load8_or_zero(dOh + q * D + 16 * c + 8 * h, ok);
+        }
+        lse2[cb] = ok ? LSE[bh * S + q] * kLog2e : 0.f;
+        dd[cb] = ok ? Dv[bh * S + q] : 0.f;
+    }
+    floatx16 acc[2][D / 32];
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) acc[cb][db] = floatx16{};
+
+    RT kr, vr;
+    CT ktr;
+    kr.load(Kh, 0, S);
+    vr.load(Vh, 0, S);
+    ktr.load(KTh, 0, a.S_pad);
+    kr.store(lds);
+    vr.store(lds + RSZ);
+    ktr.store(lds + 2 * RSZ);
+    __syncthreads();
+
+    for (int t = 0; t < ntiles; ++t) {
+        const int buf = t & 1;
+        if (t + 1 < ntiles) {
+            kr.load(Kh, (int64_t)(t + 1) * kBN, S);
+            vr.load(Vh, (int64_t)(t + 1) * kBN, S);
+            ktr.load(KTh, (int64_t)(t + 1) * kBN, a.S_pad);
+        }
+        const T* lk = lds + buf * BUF;
+        const T* lv = lk + RSZ;
+        const T* lkt = lk + 2 * RSZ;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            const int64_t kbase = (int64_t)t * kBN + 32 * ks;
+            if (kbase > q_last_w) continue;
+            floatx16 s[2] = {floatx16{}, floatx16{}}, dp[2] = {floatx16{}, floatx16{}};
+#pragma unroll
+            for (int c = 0; c < D / 16; ++c) {
+                const F kf = load8(lk + (32 * ks + col) * RT::LD + 16 * c + 8 * h);
+                const F vf = load8(lv + (32 * ks + col) * RT::LD + 16 * c + 8 * h);
+                mma_k16(s[0], kf, qf[0][c]);
+                mma_k16(s[1], kf, qf[1][c]);
+                mma_k16(dp[0], vf, df[0][c]);
+                mma_k16(dp[1], vf, df[1][c]);
+            }
+            const bool need_mask = (kbase + 31 > q_base) || (kbase + 31 >= S);
+#pragma unroll
+            for (int cb = 0; cb < 2; ++cb) {
+                const int64_t q = q_base + 32 * cb + col;
+                const bool qok = q < S;
+#pragma unroll
+                for (int j = 0; j < 16; ++j) {
+                    float p = fast_exp2(s[cb][j] * a.scale_log2 - lse2[cb]);
+                    if (need_mask) {
+                        const int64_t key = kbase + c_row(j, h);
+                        if (key > q || key >= S || !qok) p = 0.f;
+                    }
+                    s[cb][j] = p * (dp[cb][j] - dd[cb]);
+                }
+            }
+#pragma unroll
+            for (int c2 = 0; c2 < 2; ++c2) {
+                F g0, g1, r0, r1;
+                split_frag<T>(s[0], c2, g0, r0);
+                split_frag<T>(s[1], c2, g1, r1);
+#pragma unroll
+                for (int db = 0; db < D / 32; ++db) {
+                    const F kf = load_4_4(lkt + (32 * db + col) * CT::LD + 32 * ks + 16 * c2 + 4 * h);
+                    mma_k16(acc[0][db], kf, g0);
+                    mma_k16(acc[1][db], kf, g1);
+                    if (kSplitP<T>) {
+                        mma_k16(acc[0][db], kf, r0);
+                        mma_k16(acc[1][db], kf, r1);
+                    }
+                }
+            }
+        }
+        if (t + 1 < ntiles) {
+            T* nb = lds + (buf ^ 1) * BUF;
+            kr.store(nb);
+            vr.store(nb + RSZ);
+            ktr.store(nb + 2 * RSZ);
+        }
+        __syncthreads();
+    }
+
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+        const int64_t q = q_base + 32 * cb + col;
+        if (q >= S) continue;
+        OutT* row = dQ + (bh * S + q) * D;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    row[32 * db + 8 * m + 4 * h + i] = static_cast<OutT>(acc[cb][db][4 * m + i] * a.scale);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV: per 256-key block, over query tiles from the diagonal on:
+// S = Q K^T, P = exp(S - LSE), dP = dO V^T, dS = P (dP - D),
+// dV^T += dO^T P, dK^T += Q^T dS  (P and dS as bf16 hi + lo parts).
+// ---------------------------------------------------------------------------
+template <typename T, int D, typename OutT>
+__global__ __launch_bounds__(kThreads) void attn_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K,
+                                                             const T* __restrict__ V, const T* __restrict__ QT,
+                                                             const T* __restrict__ dO, const T* __restrict__ dOT,
+                                                             const float* __restrict__ LSE,
+                                                             const float* __restrict__ Dv, OutT* __restrict__ dK,
+                                                             OutT* __restrict__ dV, AttnK a) {
+    typedef typename Frag<T>::type F;
+    typedef RowTile<T, D> RT;
+    typedef ColTile<T, D> CT;
+    constexpr int RSZ = kBN * RT::LD, CSZ = D * CT::LD;
+    constexpr int BUF = 2 * RSZ + 2 * CSZ + 2 * kBN * (int)(sizeof(float) / sizeof(T));
+    extern __shared__ __align__(16) unsigned char smem[];
+    T* lds = reinterpret_cast<T*>(smem);
+
+    int64_t bh; int kb;
+    block_order(a, false, bh, kb);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int col = lane & 31, h = lane >> 5;
+    const int64_t S = a.S;
+    const T* Qh = Q + bh * S * D;
+    const T* Kh = K + bh * S * D;
+    const T* Vh = V + bh * S * D;
+    const T* QTh = QT + bh * D * a.S_pad;
+    const T* dOh = dO + bh * S * D;
+    const T* dOTh = dOT + bh * D * a.S_pad;
+    const float* LSEh = LSE + bh * S;
+    const float* Dh = Dv + bh * S;
+
+    const int64_t k_blk0 = (int64_t)kb * kBlockRows;
+    const int64_t k_base = k_blk0 + wave * kWaveRows;
+    const int t0 = (int)(k_blk0 / kBN);
+    const int ntiles_total = (int)((S + kBN - 1) / kBN);
+
+    F kf[2][D / 16], vf[2][D / 16];
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc) {
+        const int64_t key = k_base + 32 * kc + col;
+#pragma unroll
+        for (int c = 0; c < D / 16; ++c) {
+            kf[kc][c] = load8_or_zero(Kh + key * D + 16 * c + 8 * h, key < S);
+            vf[kc][c] = load8_or_zero(Vh + key * D + 16 * c + 8 * h, key < S);
+        }
+    }
+    floatx16 dk[2][D / 32], dv[2][D / 32];
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+            dk[kc][db] = floatx16{};
+            dv[kc][db] = floatx16{};
+        }
+
+    RT qr, dor;
+    CT qtr, dotr;
+    float lse_r = 0.f, d_r = 0.f;   // one query per thread for the first 64 threads
+    auto load_tile = [&](int t) {
+        const int64_t r0 = (int64_t)t * kBN;
+        qr.load(Qh, r0, S);
+        dor.load(dOh, r0, S);
+        qtr.load(QTh, r0, a.S_pad);
+        dotr.load(dOTh, r0, a.S_pad);
+        if (threadIdx.x < kBN) {
+            const int64_t q = r0 + threadIdx.x;
+            lse_r = q < S ? LSEh[q] * kLog2e : 0.f;
+            d_r = q < S ? Dh[q] : 0.f;
+        }
+    };
+    auto store_tile = [&](T* b) {
+        qr.store(b);
+        dor.store(b + RSZ);
+        qtr.store(b + 2 * RSZ);
+        dotr.store(b + 2 * RSZ + CSZ);
+        float* f = reinterpret_cast<float*>(b + 2 * RSZ + 2 * CSZ);
+        if (threadIdx.x < kBN) {
+            f[threadIdx.x] = lse_r;
+            f[kBN + threadIdx.x] = d_r;
+        }
+    };
+
+    if (t0 < ntiles_total) {
+        load_tile(t0);
+        store_tile(lds);
+    }
+    __syncthreads();
+
+    for (int t = t0; t < ntiles_total; ++t) {
+        const int buf = (t - t0) & 1;
+        if (t + 1 < ntiles_total) load_tile(t + 1);
+        const T* lq = lds + buf * BUF;
+        const T* ldo = lq + RSZ;
+        const T* lqt = lq + 2 * RSZ;
+        const T* ldot = lqt + CSZ;
+        const float* lf = reinterpret_cast<const float*>(lqt + 2 * CSZ);
+#pragma unroll
+        for (int qs = 0; qs < 2; ++qs) {
+            const int64_t q0 = (int64_t)t * kBN + 32 * qs;
+            if (k_base > q0 + 31 || k_base >= S) continue;   // every key of this wave after every query
+            F qa[D / 16], da[D / 16];
+#pragma unroll
+            for (int c = 0; c < D / 16; ++c) {
+                qa[c] = load8(lq + (32 * qs + col) * RT::LD + 16 * c + 8 * h);
+                da[c] = load8(ldo + (32 * qs + col) * RT::LD + 16 * c + 8 * h);
+            }
+            float lrow[16], drow[16];
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const floatx4 l4 = *reinterpret_cast<const floatx4*>(lf + 32 * qs + 8 * m + 4 * h);
+                const floatx4 d4 = *reinterpret_cast<const floatx4*>(lf + kBN + 32 * qs + 8 * m + 4 * h);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    lrow[4 * m + i] = l4[i];
+                    drow[4 * m + i] = d4[i];
+                }
+            }
+            floatx16 p[2], ds[2];
+#pragma unroll
+            for (int kc = 0; kc < 2; ++kc) {
+                floatx16 s = floatx16{}, dp = floatx16{};
+#pragma unroll
+                for (int c = 0; c < D / 16; ++c) {
+                    mma_k16(s, qa[c], kf[kc][c]);
+                    mma_k16(dp, da[c], vf[kc][c]);
+                }
+                const int64_t key = k_base + 32 * kc + col;
+                const bool need_mask = (k_base + 32 * kc + 31 > q0) || (q0 + 31 >= S);
+#pragma unroll
+                for (int j = 0; j < 16; ++j) {
+                    float pv = fast_exp2(s[j] * a.scale_log2 - lrow[j]);
+                    if (need_mask) {
+                        const int64_t q = q0 + c_row(j, h);
+                        if (key > q || q >= S) pv = 0.f;
+                    }
+                    p[kc][j] = pv;
+                    ds[kc][j] = pv * (dp[j] - drow[j]);
+                }
+            }
+#pragma unroll
+            for (int c2 = 0; c2 < 2; ++c2) {
+                F p0, p1, g0, g1, p0r, p1r, g0r, g1r;
+                split_frag<T>(p[0], c2, p0, p0r);
+                split_frag<T>(p[1], c2, p1, p1r);
+                split_frag<T>(ds[0], c2, g0, g0r);
+                split_frag<T>(ds[1], c2, g1, g1r);
+#pragma unroll
+                for (int db = 0; db < D / 32; ++db) {
+                    const F dof = load_4_4(ldot + (32 * db + col) * CT::LD + 32 * qs + 16 * c2 + 4 * h);
+                    const F qtf = load_4_4(lqt + (32 * db + col) * CT::LD + 32 * qs + 16 * c2 + 4 * h);
+                    mma_k16(dv[0][db], dof, p0);
+                    mma_k16(dv[1][db], dof, p1);
+                    mma_k16(dk[0][db], qtf, g0);
+                    mma_k16(dk[1][db], qtf, g1);
+                    if (kSplitP<T>) {
+                        mma_k16(dv[0][db], dof, p0r);
+                        mma_k16(dv[1][db], dof, p1r);
+                        mma_k16(dk[0][db], qtf, g0r);
+                        mma_k16(dk[1][db], qtf, g1r);
+                    }
+                }
+            }
+        }
+        if (t + 1 < ntiles_total) store_tile(lds + (buf ^ 1) * BUF);
+        __syncthreads();
+    }
+
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc) {
+        const int64_t key = k_base + 32 * kc + col;
+        if (key >= S) continue;
+        OutT* rk = dK + (bh * S + key) * D;
+        OutT* rv = dV + (bh * S + key) * D;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    rk[32 * db + 8 * m + 4 * h + i] = static_cast<OutT>(dk[kc][db][4 * m + i] * a.scale);
+                    rv[32 * db + 8 * m + 4 * h + i] = static_cast<OutT>(dv[kc][db][4 * m + i]);
+                }
+    }
+}
+
+template <typename T, int D>
+size_t fwd_lds() { return 2 * (kBN * RowTile<T, D>::LD + D * ColTile<T, D>::LD) * sizeof(T); }
+template <typename T, int D>
+size_t dq_lds() { return 2 * (2 * kBN * RowTile<T, D>::LD + D * ColTile<T, D>::LD) * sizeof(T); }
+template <typename T, int D>
+size_t dkdv_lds() {
+    return 2 * ((2 * kBN * RowTile<T, D>::LD + 2 * D * ColTile<T, D>::LD) * sizeof(T) + 2 * kBN * sizeof(float));
+}
+
+AttnK make_k(const AttnArgs& a) {
+    AttnK k{};
+    k.BH = a.BH; k.S = a.S; k.S_pad = a.S_pad; k.scale = a.scale; k.scale_log2 = a.scale * kLog2e;
+    k.nblk = (int)((a.S + kBlockRows - 1) / kBlockRows);
+    return k;
+}
+
+template <typename T, int D>
+hipError_t fwd_t(const AttnArgs& a, const void* Q, const void* K, const void* VT, float* O32, void* Ot, float* lse,
+                 hipStream_t st) {
+    const AttnK k = make_k(a);
+    const size_t sh = fwd_lds<T, D>();
+    static const hipError_t attr =
+        hipFuncSetAttribute((const void*)attn_fwd_kernel<T, D>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sh);
+    (void)attr;
+    attn_fwd_kernel<T, D><<<dim3((unsigned)(k.nblk * a.BH)), kThreads, sh, st>>>(
+        (const T*)Q, (const T*)K, (const T*)VT, O32, (T*)Ot, lse, k);
+    return hipGetLastError();
+}
+
+template <typename T, int D, typename OutT>
+hipError_t bwd_t(const AttnArgs& a, const void* Q, const void* K, const void* V, const void* QT, const void* KT,
+                 const void* dO, const void* dOT, const float* lse, const float* Dv, void* dQ, void* dK, void* dV,
+                 hipStream_t st) {
+    const AttnK k = make_k(a);
+    const size_t sh1 = dkdv_lds<T, D>();
+    static const hipError_t attr1 = hipFuncSetAttribute((const void*)attn_dkdv_kernel<T, D, OutT>,
+                                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)sh1);
+    (void)attr1;
+    attn_dkdv_kernel<T, D, OutT><<<dim3((unsigned)(k.nblk * a.BH)), kThreads, sh1, st>>>(
+        (const T*)Q, (const T*)K, (const T*)V, (const T*)QT, (const T*)dO, (const T*)dOT, lse, Dv, (OutT*)dK,
+        (OutT*)dV, k);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const size_t sh2 = dq_lds<T, D>();
+    static const hipError_t attr2 = hipFuncSetAttribute((const void*)attn_dq_kernel<T, D, OutT>,
+                                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)sh2);
+    (void)attr2;
+    attn_dq_kernel<T, D, OutT><<<dim3((unsigned)(k.nblk * a.BH)), kThreads, sh2, st>>>(
+        (const T*)Q, (const T*)K, (const T*)V, (const T*)KT, (const T*)dO, lse, Dv, (OutT*)dQ, k);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_attn_fwd(const AttnArgs& a, int dtype, const void* Q, const void* K, const void* VT, float* O32,
+                           void* Ot, float* lse, hipStream_t st) {
+    if (dtype == LH_BF16)
+        return a.d == 64 ? fwd_t<bf16, 64>(a, Q, K, VT, O32, Ot, lse, st) : fwd_t<bf16, 128>(a, Q, K, VT, O32, Ot, lse, st);
+    return fwd_t<float, 64>(a, Q, K, VT, O32, Ot, lse, st);   // f32 is built for d = 64 only
+}
+
+hipError_t launch_attn_bwd(const AttnArgs& a, int dtype, bool out_f32, const void* Q, const void* K, const void* V,
+                           const void* QT, const void* KT, const void* dO, const void* dOT, const float* lse,
+                           const float* Dv, void* dQ, void* dK, void* dV, hipStream_t st) {
+#define LH_BWD(T, D, O) bwd_t<T, D, O>(a, Q, K, V, QT, KT, dO, dOT, lse, Dv, dQ, dK, dV, st)
+    if (dtype == LH_BF16) {
+        if (a.d == 64) return out_f32 ? LH_BWD(bf16, 64, float) : LH_BWD(bf16, 64, bf16);
+        return out_f32 ? LH_BWD(bf16, 128, float) : LH_BWD(bf16, 128, bf16);
+    }
+    return LH_BWD(float, 64, float);   // f32 is built for d = 64 only
+#undef LH_BWD
+}

@@ -1,0 +1,83 @@
+// Device-side building blocks for the Lighthouse kernels on gfx950 (CDNA4).
+//
+// Matrix-core conventions (checked on the device: lane layouts of
+// v_mfma_f32_32x32x16_bf16 and v_mfma_f32_32x32x2_f32):
+//   A operand (32 x 16 slice of a row-major A): lane l holds A[l % 32][8*(l/32) + e], e = 0..7
+//   B operand (16 x 32):                        lane l holds B[8*(l/32) + e][l % 32]
+//   C/D (32 x 32, 16 floats per lane):          reg j holds C[8*(j/4) + 4*(l/32) + (j%4)][l % 32]
+// A "k16 step" contracts 16 k-indices: one bf16 MFMA, or eight f32 MFMAs (f32
+// step j contracts the two k-indices {j, 8 + j} of the same fragments).
+//
+// Because the k-index order of one step is free, a C tile produced by one MFMA
+// can be fed back as the B operand of the next without moving data between
+// lanes: rows 16c + {4h..4h+3, 8+4h..8+4h+3} of the C tile (c = 0, 1; h = l/32)
+// are exactly registers 8c..8c+7 of lane l, so the matching A operand reads
+// those same k-indices (two runs of four) -- see a_frag_perm().
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef float floatx8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+template <typename T> struct Frag;
+template <> struct Frag<bf16> { typedef bf16x8 type; typedef bf16x4 half; };
+template <> struct Frag<float> { typedef floatx8 type; typedef floatx4 half; };
+
+__device__ __forceinline__ void mma_k16(floatx16& acc, const bf16x8& a, const bf16x8& b) {
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
+}
+__device__ __forceinline__ void mma_k16(floatx16& acc, const floatx8& a, const floatx8& b) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[j], b[j], acc, 0, 0, 0);
+}
+
+// Eight consecutive elements (16 B for bf16, 32 B for f32).
+template <typename T>
+__device__ __forceinline__ typename Frag<T>::type load8(const T* p) {
+    return *reinterpret_cast<const typename Frag<T>::type*>(p);
+}
+template <typename T>
+__device__ __forceinline__ typename Frag<T>::type load8_or_zero(const T* p, bool ok) {
+    typename Frag<T>::type z = {};
+    return ok ? *reinterpret_cast<const typename Frag<T>::type*>(p) : z;
+}
+// Two runs of four consecutive elements at p and p + 8 (the permuted k order).
+template <typename T>
+__device__ __forceinline__ typename Frag<T>::type load_4_4(const T* p) {
+    typedef typename Frag<T>::half H;
+    H lo = *reinterpret_cast<const H*>(p);
+    H hi = *reinterpret_cast<const H*>(p + 8);
+    typename Frag<T>::type r;
+    r.lo = lo;
+    r.hi = hi;
+    return r;
+}
+
+// Registers 8c .. 8c+7 of a C tile as a B-operand fragment of type T.
+template <typename T>
+__device__ __forceinline__ typename Frag<T>::type c_to_frag(const floatx16& c, int cc) {
+    typename Frag<T>::type r;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) r[e] = static_cast<T>(c[8 * cc + e]);
+    return r;
+}
+
+// Row (within a 32-row C tile) held by register j of lane-half h.
+__device__ __forceinline__ int c_row(int j, int h) { return 8 * (j >> 2) + 4 * h + (j & 3); }
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+template <typename T> __device__ __forceinline__ float to_f(T x) { return static_cast<float>(x); }
+
+// Wave-wide helpers (wave64).
+__device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
+
+// Sixteen bytes of T.
+template <typename T> struct V16;
+template <> struct V16<bf16> { typedef bf16x8 type; enum { N = 8 }; };
+template <> struct V16<float> { typedef floatx4 type; enum { N = 4 }; };

@@ -1,0 +1,56 @@
+// Internal launch interface between the C-ABI layer (lh_api.hip) and the
+// kernel translation units.  Every launcher only enqueues on `st`.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/lighthouse.h"
+
+struct LhGeom {
+    int64_t BH, N, d, S, S_pad, M_total, Mu;   // Mu = M_total - N (rows above level 0)
+    int p, L;
+    int64_t M[LH_MAX_LEVELS];
+    int64_t k_eff[LH_MAX_LEVELS];
+    int64_t off[LH_MAX_LEVELS + 1];           // level offsets (flat ids)
+    int64_t pw[LH_MAX_LEVELS];                // p^l
+    int64_t words_off[LH_MAX_LEVELS + 1];     // bitmap word offset of level l (l >= 1)
+    int64_t words_total;                      // per head
+};
+
+// selection-side kernels (lh_select.hip)
+hipError_t launch_pool(const LhGeom& g, int dtype, const void* q, const void* k, const void* v, void* pyr,
+                       hipStream_t st);
+hipError_t launch_scores(const LhGeom& g, int dtype, const void* q, const void* k, float* sigma,
+                         hipStream_t st);
+hipError_t launch_topk(const LhGeom& g, const float* sigma, uint32_t* words, int32_t* prefix, hipStream_t st);
+hipError_t launch_map(const LhGeom& g, const uint32_t* words, const int32_t* prefix, int32_t* gidx,
+                      int32_t* gpos, hipStream_t st);
+
+// data movement (lh_scatter.hip)
+hipError_t launch_gather(const LhGeom& g, int dtype, const void* q, const void* k, const void* v,
+                         const void* pyr, const int32_t* gidx, void* const rows[3], void* const cols[3],
+                         hipStream_t st);
+// og: the sub-sequence output, kept in f32 [BH,S,d]
+hipError_t launch_scatter_fwd(const LhGeom& g, int dtype, const float* og, const int32_t* gpos, void* o,
+                              hipStream_t st);
+hipError_t launch_scatter_bwd(const LhGeom& g, int dtype, const void* dout, const float* og,
+                              const int32_t* gidx, void* dog, void* dogT, float* Dv, hipStream_t st);
+hipError_t launch_gather_pool_bwd(const LhGeom& g, int dtype, const float* const dx_g[3], const int32_t* gpos,
+                                  void* const dx[3], hipStream_t st);
+hipError_t launch_transpose(int dtype, int64_t BH, int64_t S, int64_t S_pad, int64_t d, const void* x,
+                            void* xT, hipStream_t st);
+hipError_t launch_dense_bwd_prep(int dtype, int64_t BH, int64_t S, int64_t S_pad, int64_t d, const void* dout,
+                                 const float* o32, void* doT, float* Dv, hipStream_t st);
+
+// attention (lh_attention.hip)
+struct AttnArgs {
+    int64_t BH, S, S_pad, d;
+    float scale;
+};
+// O32: f32 output [BH,S,d] (always); Ot: optional copy in the input dtype (may be null)
+hipError_t launch_attn_fwd(const AttnArgs& a, int dtype, const void* Q, const void* K, const void* VT, float* O32,
+                           void* Ot, float* lse, hipStream_t st);
+// out_f32: dq/dk/dv are f32 (true) or the input dtype (false)
+hipError_t launch_attn_bwd(const AttnArgs& a, int dtype, bool out_f32, const void* Q, const void* K,
+                           const void* V, const void* QT, const void* KT, const void* dO, const void* dOT,
+                           const float* lse, const float* Dv, void* dQ, void* dK, void* dV, hipStream_t st);

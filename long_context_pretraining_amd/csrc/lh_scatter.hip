@@ -1,0 +1,371 @@
+// Data movement around the sub-sequence attention of Lighthouse Attention on
+// gfx950: gather of the selected triples (page "skillsmp.com ...
+// lighthouse-attention", Stage 3; gist.science Methodology 2C), scatter-back
+// over R(l, i) (skill card, Stage 4), and the backward of both (skill card,
+// gradient flow).  All HBM-bound: 16-byte coalesced rows, LDS-staged
+// transposes, and pull formulations (each output row reads its <= L sources)
+// so no atomics and bit-reproducible results.
+#include "lh_device.h"
+#include "lh_internal.h"
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kRows = 64;   // rows (slots or tokens) per block
+
+struct MapGeo {
+    int64_t BH, N, d, S, S_pad, Mu, M_total;
+    int p, L;
+    int64_t off[LH_MAX_LEVELS + 1];
+    int64_t pw[LH_MAX_LEVELS];
+};
+
+MapGeo make_geo(const LhGeom& g) {
+    MapGeo m{};
+    m.BH = g.BH; m.N = g.N; m.d = g.d; m.S = g.S; m.S_pad = g.S_pad; m.Mu = g.Mu; m.M_total = g.M_total;
+    m.p = g.p; m.L = g.L;
+    for (int l = 0; l <= g.L; ++l) m.off[l] = g.off[l];
+    for (int l = 0; l < g.L; ++l) m.pw[l] = g.pw[l];
+    return m;
+}
+
+__device__ __forceinline__ int level_of(const MapGeo& G, int64_t flat) {
+    int l = 0;
+    while (flat >= G.off[l + 1]) ++l;
+    return l;
+}
+
+// Write the [kRows x d] tile held in LDS (row stride d + pad) as columns
+// s0 .. s0+63 of the transposed array xT [d][S_pad].
+template <typename T>
+__device__ __forceinline__ void store_transposed(const T* tile, int ld, int64_t d, T* xT, int64_t S_pad,
+                                                 int64_t s0) {
+    constexpr int VEC = V16<T>::N;
+    typedef typename V16<T>::type VT;
+    const int per_row = kRows / VEC;
+    for (int task = threadIdx.x; task < d * per_row; task += kThreads) {
+        const int dim = task / per_row, cv = task - dim * per_row;
+        VT out;
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) out[i] = tile[(cv * VEC + i) * ld + dim];
+        *reinterpret_cast<VT*>(xT + dim * S_pad + s0 + cv * VEC) = out;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Gather: rows of the selected entries in slot order, row-major [S][d] and
+// transposed [d][S_pad] (columns past S are zero).  Level 0 rows come from
+// the input, coarser ones from the pyramid (pyramid row = flat id - N).
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(kThreads) void gather_kernel(const T* __restrict__ q, const T* __restrict__ k,
+                                                          const T* __restrict__ v, const T* __restrict__ pyr,
+                                                          const int32_t* __restrict__ gidx, T* r0, T* r1, T* r2,
+                                                          T* c0, T* c1, T* c2, MapGeo G) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    T* tile = reinterpret_cast<T*>(smem);
+    constexpr int VEC = V16<T>::N;
+    typedef typename V16<T>::type VT;
+    const int z = blockIdx.z;
+    const T* src0 = z == 0 ? q : (z == 1 ? k : v);
+    const T* srcp = pyr + (int64_t)z * G.BH * G.Mu * G.d;
+    T* rows = z == 0 ? r0 : (z == 1 ? r1 : r2);
+    T* cols = z == 0 ? c0 : (z == 1 ? c1 : c2);
+    const int64_t bh = blockIdx.y, s0 = (int64_t)blockIdx.x * kRows;
+    const int ld = (int)G.d + VEC;
+    const int nvec = (int)(G.d / VEC);
+    for (int task = threadIdx.x; task < kRows * nvec; task += kThreads) {
+        const int sl = task / nvec, vv = task - sl * nvec;
+        const int64_t s = s0 + sl;
+        VT val = {};
+        const int64_t flat = s < G.S ? gidx[bh * G.S + s] : -1;
+        if (flat >= 0 && flat < G.M_total) {   // a map entry outside the pyramid gathers zeros
+            const T* src = flat < G.N ? src0 + (bh * G.N + flat) * G.d : srcp + (bh * G.Mu + flat - G.N) * G.d;
+            val = *reinterpret_cast<const VT*>(src + vv * VEC);
+            *reinterpret_cast<VT*>(rows + (bh * G.S + s) * G.d + vv * VEC) = val;
+        }
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) tile[sl * ld + vv * VEC + i] = val[i];
+    }
+    __syncthreads();
+    store_transposed(tile, ld, G.d, cols + bh * G.d * G.S_pad, G.S_pad, s0);
+}
+
+// ---------------------------------------------------------------------------
+// Scatter forward (pull): o[t] = sum_l Og[gpos(l, floor((t+1)/p^l) - 1)],
+// levels ascending, in f32 from the f32 sub-sequence output, one rounding to
+// T; 0 where no selected entry covers t.
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(kThreads) void scatter_fwd_kernel(const float* __restrict__ og,
+                                                               const int32_t* __restrict__ gpos,
+                                                               T* __restrict__ o, MapGeo G) {
+    typedef typename Frag<T>::type OV;
+    const int64_t bh = blockIdx.y, t0 = (int64_t)blockIdx.x * kRows;
+    const int nvec = (int)(G.d / 8);
+    const int32_t* gp = gpos + bh * G.M_total;
+    for (int task = threadIdx.x; task < kRows * nvec; task += kThreads) {
+        const int tl = task / nvec, vv = task - tl * nvec;
+        const int64_t t = t0 + tl;
+        if (t >= G.N) continue;
+        floatx8 acc = {};
+        for (int l = 0; l < G.L; ++l) {
+            const int64_t i = (t + 1) / G.pw[l] - 1;
+            if (i < 0) continue;
+            const int64_t g = gp[G.off[l] + i];
+            if (g < 0 || g >= G.S) continue;
+            acc += *reinterpret_cast<const floatx8*>(og + (bh * G.S + g) * G.d + vv * 8);
+        }
+        OV out;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) out[e] = static_cast<T>(acc[e]);
+        *reinterpret_cast<OV*>(o + (bh * G.N + t) * G.d + vv * 8) = out;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Scatter backward: dOg[g] = sum of dout over R(l, i) (clipped at N-1) for
+// the entry in slot g, summed in token order in f32 and stored in T; also its
+// transpose and D[g] = dOg[g] . Og[g] (f32), which the attention backward
+// needs.
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(kThreads) void scatter_bwd_kernel(const T* __restrict__ dout,
+                                                               const float* __restrict__ og,
+                                                               const int32_t* __restrict__ gidx, T* dog, T* dogT,
+                                                               float* __restrict__ Dv, MapGeo G) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    constexpr int VEC = V16<T>::N;
+    typedef typename V16<T>::type VT;
+    const int ld = (int)G.d + VEC;
+    const int nvec = (int)(G.d / VEC);
+    T* tile = reinterpret_cast<T*>(smem);
+    float* dpart = reinterpret_cast<float*>(smem + sizeof(T) * kRows * ld);
+    const int64_t bh = blockIdx.y, s0 = (int64_t)blockIdx.x * kRows;
+    for (int task = threadIdx.x; task < kRows * nvec; task += kThreads) {
+        const int sl = task / nvec, vv = task - sl * nvec;
+        const int64_t s = s0 + sl;
+        VT r = {};
+        float dp = 0.f;
+        const int64_t flat = s < G.S ? gidx[bh * G.S + s] : -1;
+        if (flat >= 0 && flat < G.M_total) {
+            const int l = level_of(G, flat);
+            const int64_t i = flat - G.off[l];
+            const int64_t lo = (i + 1) * G.pw[l] - 1;
+            const int64_t hi = (lo + G.pw[l] - 1) < (G.N - 1) ? (lo + G.pw[l] - 1) : (G.N - 1);
+            float acc[VEC];
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) acc[e] = 0.f;
+            for (int64_t t = lo; t <= hi; ++t) {
+                const VT x = *reinterpret_cast<const VT*>(dout + (bh * G.N + t) * G.d + vv * VEC);
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) acc[e] += to_f(x[e]);
+            }
+            const float* ov = og + (bh * G.S + s) * G.d + vv * VEC;
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) {
+                r[e] = static_cast<T>(acc[e]);
+                dp += to_f(r[e]) * ov[e];
+            }
+        }
+        if (s < G.S) *reinterpret_cast<VT*>(dog + (bh * G.S + s) * G.d + vv * VEC) = r;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) tile[sl * ld + vv * VEC + e] = r[e];
+        dpart[sl * nvec + vv] = dp;
+    }
+    __syncthreads();
+    for (int sl = threadIdx.x; sl < kRows; sl += kThreads) {
+        const int64_t s = s0 + sl;
+        if (s < G.S) {
+            float acc = 0.f;
+            for (int vv = 0; vv < nvec; ++vv) acc += dpart[sl * nvec + vv];
+            Dv[bh * G.S + s] = acc;
+        }
+    }
+    store_transposed(tile, ld, G.d, dogT + bh * G.d * G.S_pad, G.S_pad, s0);
+}
+
+// ---------------------------------------------------------------------------
+// Gather + pooling backward (pull): dX[t] = sum_l dXg[gpos(l, floor(t/p^l))] / p^l
+// over selected entries, levels ascending, f32, stored in T.
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(kThreads) void gpool_bwd_kernel(const float* __restrict__ g0,
+                                                             const float* __restrict__ g1,
+                                                             const float* __restrict__ g2,
+                                                             const int32_t* __restrict__ gpos, T* o0, T* o1, T* o2,
+                                                             MapGeo G) {
+    const int z = blockIdx.z;
+    const float* dxg = z == 0 ? g0 : (z == 1 ? g1 : g2);
+    T* out = z == 0 ? o0 : (z == 1 ? o1 : o2);
+    const int64_t bh = blockIdx.y, t0 = (int64_t)blockIdx.x * kRows;
+    const int nvec = (int)(G.d / 8);
+    const int32_t* gp = gpos + bh * G.M_total;
+    for (int task = threadIdx.x; task < kRows * nvec; task += kThreads) {
+        const int tl = task / nvec, vv = task - tl * nvec;
+        const int64_t t = t0 + tl;
+        if (t >= G.N) continue;
+        float acc[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+        for (int l = 0; l < G.L; ++l) {
+            const int64_t g = gp[G.off[l] + t / G.pw[l]];
+            if (g < 0 || g >= G.S) continue;
+            const floatx8 x = *reinterpret_cast<const floatx8*>(dxg + (bh * G.S + g) * G.d + vv * 8);
+            const float den = (float)G.pw[l];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[e] += x[e] / den;
+        }
+        typename Frag<T>::type r;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) r[e] = static_cast<T>(acc[e]);
+        *reinterpret_cast<typename Frag<T>::type*>(out + (bh * G.N + t) * G.d + vv * 8) = r;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Dense-baseline helpers: transpose x [S][d] -> xT [d][S_pad] (zero columns
+// past S), and the backward prologue (transposed dO and D = rowsum(dO * O)).
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(kThreads) void transpose_kernel(const T* __restrict__ x, T* xT, int64_t S,
+                                                             int64_t S_pad, int64_t d) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    T* tile = reinterpret_cast<T*>(smem);
+    constexpr int VEC = V16<T>::N;
+    typedef typename V16<T>::type VT;
+    const int ld = (int)d + VEC, nvec = (int)(d / VEC);
+    const int64_t bh = blockIdx.y, s0 = (int64_t)blockIdx.x * kRows;
+    for (int task = threadIdx.x; task < kRows * nvec; task += kThreads) {
+        const int sl = task / nvec, vv = task - sl * nvec;
+        VT val = {};
+        if (s0 + sl < S) val = *reinterpret_cast<const VT*>(x + (bh * S + s0 + sl) * d + vv * VEC);
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) tile[sl * ld + vv * VEC + i] = val[i];
+    }
+    __syncthreads();
+    store_transposed(tile, ld, d, xT + bh * d * S_pad, S_pad, s0);
+}
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void dense_prep_kernel(const T* __restrict__ dout, const float* __restrict__ o,
+                                                              T* doT, float* __restrict__ Dv, int64_t S,
+                                                              int64_t S_pad, int64_t d) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    constexpr int VEC = V16<T>::N;
+    typedef typename V16<T>::type VT;
+    const int ld = (int)d + VEC, nvec = (int)(d / VEC);
+    T* tile = reinterpret_cast<T*>(smem);
+    float* dpart = reinterpret_cast<float*>(smem + sizeof(T) * kRows * ld);
+    const int64_t bh = blockIdx.y, s0 = (int64_t)blockIdx.x * kRows;
+    for (int task = threadIdx.x; task < kRows * nvec; task += kThreads) {
+        const int sl = task / nvec, vv = task - sl * nvec;
+        VT val = {};
+        float dp = 0.f;
+        if (s0 + sl < S) {
+            val = *reinterpret_cast<const VT*>(dout + (bh * S + s0 + sl) * d + vv * VEC);
+            const float* ov = o + (bh * S + s0 + sl) * d + vv * VEC;
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) dp += to_f(val[e]) * ov[e];
+        }
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) tile[sl * ld + vv * VEC + i] = val[i];
+        dpart[sl * nvec + vv] = dp;
+    }
+    __syncthreads();
+    for (int sl = threadIdx.x; sl < kRows; sl += kThreads) {
+        if (s0 + sl < S) {
+            float acc = 0.f;
+            for (int vv = 0; vv < nvec; ++vv) acc += dpart[sl * nvec + vv];
+            Dv[bh * S + s0 + sl] = acc;
+        }
+    }
+    store_transposed(tile, ld, d, doT + bh * d * S_pad, S_pad, s0);
+}
+
+inline unsigned blocks_for(int64_t n) { return (unsigned)((n + kRows - 1) / kRows); }
+
+template <typename T> size_t tile_bytes(int64_t d) { return sizeof(T) * kRows * (d + V16<T>::N); }
+
+}  // namespace
+
+hipError_t launch_gather(const LhGeom& g, int dtype, const void* q, const void* k, const void* v, const void* pyr,
+                         const int32_t* gidx, void* const rows[3], void* const cols[3], hipStream_t st) {
+    const MapGeo G = make_geo(g);
+    dim3 grid((unsigned)(g.S_pad / kRows), (unsigned)g.BH, 3);
+    if (dtype == LH_BF16)
+        gather_kernel<bf16><<<grid, kThreads, tile_bytes<bf16>(g.d), st>>>(
+            (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)pyr, gidx, (bf16*)rows[0], (bf16*)rows[1],
+            (bf16*)rows[2], (bf16*)cols[0], (bf16*)cols[1], (bf16*)cols[2], G);
+    else
+        gather_kernel<float><<<grid, kThreads, tile_bytes<float>(g.d), st>>>(
+            (const float*)q, (const float*)k, (const float*)v, (const float*)pyr, gidx, (float*)rows[0],
+            (float*)rows[1], (float*)rows[2], (float*)cols[0], (float*)cols[1], (float*)cols[2], G);
+    return hipGetLastError();
+}
+
+hipError_t launch_scatter_fwd(const LhGeom& g, int dtype, const float* og, const int32_t* gpos, void* o,
+                              hipStream_t st) {
+    const MapGeo G = make_geo(g);
+    dim3 grid(blocks_for(g.N), (unsigned)g.BH);
+    if (dtype == LH_BF16)
+        scatter_fwd_kernel<bf16><<<grid, kThreads, 0, st>>>(og, gpos, (bf16*)o, G);
+    else
+        scatter_fwd_kernel<float><<<grid, kThreads, 0, st>>>(og, gpos, (float*)o, G);
+    return hipGetLastError();
+}
+
+hipError_t launch_scatter_bwd(const LhGeom& g, int dtype, const void* dout, const float* og, const int32_t* gidx,
+                              void* dog, void* dogT, float* Dv, hipStream_t st) {
+    const MapGeo G = make_geo(g);
+    dim3 grid((unsigned)(g.S_pad / kRows), (unsigned)g.BH);
+    if (dtype == LH_BF16) {
+        const size_t sh = tile_bytes<bf16>(g.d) + 4 * kRows * (g.d / 8);
+        scatter_bwd_kernel<bf16><<<grid, kThreads, sh, st>>>((const bf16*)dout, og, gidx, (bf16*)dog,
+                                                              (bf16*)dogT, Dv, G);
+    } else {
+        const size_t sh = tile_bytes<float>(g.d) + 4 * kRows * (g.d / 4);
+        scatter_bwd_kernel<float><<<grid, kThreads, sh, st>>>((const float*)dout, og, gidx,
+                                                               (float*)dog, (float*)dogT, Dv, G);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_gather_pool_bwd(const LhGeom& g, int dtype, const float* const dx_g[3], const int32_t* gpos,
+                                  void* const dx[3], hipStream_t st) {
+    const MapGeo G = make_geo(g);
+    dim3 grid(blocks_for(g.N), (unsigned)g.BH, 3);
+    if (dtype == LH_BF16)
+        gpool_bwd_kernel<bf16><<<grid, kThreads, 0, st>>>(dx_g[0], dx_g[1], dx_g[2], gpos, (bf16*)dx[0],
+                                                          (bf16*)dx[1], (bf16*)dx[2], G);
+    else
+        gpool_bwd_kernel<float><<<grid, kThreads, 0, st>>>(dx_g[0], dx_g[1], dx_g[2], gpos, (float*)dx[0],
+                                                           (float*)dx[1], (float*)dx[2], G);
+    return hipGetLastError();
+}
+
+hipError_t launch_transpose(int dtype, int64_t BH, int64_t S, int64_t S_pad, int64_t d, const void* x, void* xT,
+                            hipStream_t st) {
+    dim3 grid((unsigned)(S_pad / kRows), (unsigned)BH);
+    if (dtype == LH_BF16)
+        transpose_kernel<bf16><<<grid, kThreads, tile_bytes<bf16>(d), st>>>((const bf16*)x, (bf16*)xT, S, S_pad, d);
+    else
+        transpose_kernel<float><<<grid, kThreads, tile_bytes<float>(d), st>>>((const float*)x, (float*)xT, S, S_pad,
+                                                                              d);
+    return hipGetLastError();
+}
+
+hipError_t launch_dense_bwd_prep(int dtype, int64_t BH, int64_t S, int64_t S_pad, int64_t d, const void* dout,
+                                 const float* o, void* doT, float* Dv, hipStream_t st) {
+    dim3 grid((unsigned)(S_pad / kRows), (unsigned)BH);
+    if (dtype == LH_BF16) {
+        const size_t sh = tile_bytes<bf16>(d) + 4 * kRows * (d / 8);
+        dense_prep_kernel<bf16><<<grid, kThreads, sh, st>>>((const bf16*)dout, o, (bf16*)doT, Dv, S,
+                                                             S_pad, d);
+    } else {
+        const size_t sh = tile_bytes<float>(d) + 4 * kRows * (d / 4);
+        dense_prep_kernel<float><<<grid, kThreads, sh, st>>>((const float*)dout, o, (float*)doT, Dv, S,
+                                                              S_pad, d);
+    }
+    return hipGetLastError();
+}

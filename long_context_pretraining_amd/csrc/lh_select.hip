@@ -1,0 +1,446 @@
+// Stage 1 and 2 of Lighthouse Attention on gfx950: the mean pyramid, the
+// l2-norm token scores with max-pool inheritance, the exact per-level top-K,
+// and the gather map (page "skillsmp.com ... lighthouse-attention", Stage 1-3;
+// gist.science technical summary, Methodology 2A-2C).
+//
+// All of these are bandwidth- or latency-bound; nothing here is a dense
+// contraction, so no matrix cores: coalesced 16-byte loads, LDS staging of the
+// coarser levels, and wave shuffles for the per-token reductions.
+#include "lh_device.h"
+#include "lh_internal.h"
+
+namespace {
+
+constexpr int kThreads = 256;
+
+// ---------------------------------------------------------------------------
+// Pyramid: level l entry i = (sum of the p children of level l-1, index
+// order, f32) / p; the recursion keeps f32 values, each stored level is one
+// rounding to T.  One block = a chunk of tokens (a multiple of p^(L-1)) times
+// a slice of DS dimensions; the f32 levels of the chunk stay in LDS.
+// ---------------------------------------------------------------------------
+struct PoolP {
+    int64_t N, d, BH, Mu;
+    int p, L, chunk, DS, nslices;
+    int64_t offu[LH_MAX_LEVELS];  // row of level l inside a head's pyramid block
+    int64_t pw[LH_MAX_LEVELS];
+};
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void pool_kernel(const T* __restrict__ x0, const T* __restrict__ x1,
+                                                        const T* __restrict__ x2, T* __restrict__ pyr, PoolP P) {
+    extern __shared__ float lds[];
+    constexpr int VEC = V16<T>::N;
+    typedef typename V16<T>::type VT;
+    const T* x = blockIdx.z == 0 ? x0 : (blockIdx.z == 1 ? x1 : x2);
+    const int slice = blockIdx.x % P.nslices;
+    const int64_t c0 = (int64_t)(blockIdx.x / P.nslices) * P.chunk;
+    const int64_t len = (P.N - c0) < P.chunk ? (P.N - c0) : P.chunk;
+    const int64_t bh = blockIdx.y;
+    const int dim0 = slice * P.DS;
+    const int nvec = P.DS / VEC;
+    const T* xh = x + bh * P.N * P.d;
+    T* ph = pyr + ((int64_t)blockIdx.z * P.BH + bh) * P.Mu * P.d;
+
+    int prev_off = 0, cur_off = 0;
+    int64_t n_prev = len;
+    for (int l = 1; l < P.L; ++l) {
+        const int n = (int)(n_prev / P.p);
+        const int64_t e0 = c0 / P.pw[l];
+        for (int task = threadIdx.x; task < n * nvec; task += kThreads) {
+            const int e = task / nvec, vv = task - e * nvec;
+            float acc[VEC];
+#pragma unroll
+            for (int i = 0; i < VEC; ++i) acc[i] = 0.f;
+            for (int c = 0; c < P.p; ++c) {
+                if (l == 1) {
+                    const VT v = *reinterpret_cast<const VT*>(xh + (c0 + (int64_t)e * P.p + c) * P.d + dim0 + vv * VEC);
+#pragma unroll
+                    for (int i = 0; i < VEC; ++i) acc[i] += to_f(v[i]);
+                } else {
+                    const float* src = lds + prev_off + (e * P.p + c) * P.DS + vv * VEC;
+#pragma unroll
+                    for (int i = 0; i < VEC; ++i) acc[i] += src[i];
+                }
+            }
+            VT out;
+#pragma unroll
+            for (int i = 0; i < VEC; ++i) {
+                acc[i] = acc[i] / (float)P.p;
+                out[i] = static_cast<T>(acc[i]);
+            }
+            if (l + 1 < P.L) {
+                float* dst = lds + cur_off + e * P.DS + vv * VEC;
+#pragma unroll
+                for (int i = 0; i < VEC; ++i) dst[i] = acc[i];
+            }
+            *reinterpret_cast<VT*>(ph + (P.offu[l] + e0 + e) * P.d + dim0 + vv * VEC) = out;
+        }
+        __syncthreads();
+        prev_off = cur_off;
+        cur_off += n * P.DS;
+        n_prev = n;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Scores: s_t = sqrt(SS(q_t)) + sqrt(SS(k_t)), f32.  Eight lanes per token;
+// lane r sums the squares of elements [r*d/8, (r+1)*d/8) left to right (the
+// product is rounded before the add: no contraction), then the xor-4, xor-2,
+// xor-1 butterflies give (a_r + a_{r+4}), (t_r + t_{r+2}), (u_0 + u_1).
+// Levels >= 1 take the max over their children (exact).
+// ---------------------------------------------------------------------------
+struct ScoreP {
+    int64_t N, d, BH, Mu;
+    int p, L, chunk;
+    int64_t offu[LH_MAX_LEVELS];
+    int64_t pw[LH_MAX_LEVELS];
+};
+
+template <typename T>
+__device__ __forceinline__ float sumsq_lane(const T* __restrict__ row, int cw) {
+#pragma clang fp contract(off)
+    constexpr int VEC = V16<T>::N;
+    typedef typename V16<T>::type VT;
+    float a = 0.f;
+    for (int j = 0; j < cw; j += VEC) {
+        const VT v = *reinterpret_cast<const VT*>(row + j);
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) {
+            const float x = to_f(v[i]);
+            const float sq = x * x;
+            a = a + sq;
+        }
+    }
+    return a;
+}
+
+__device__ __forceinline__ float tree8(float a) {
+#pragma clang fp contract(off)
+    const float t = a + __shfl_xor(a, 4, 64);
+    const float u = t + __shfl_xor(t, 2, 64);
+    return u + __shfl_xor(u, 1, 64);
+}
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void score_kernel(const T* __restrict__ q, const T* __restrict__ k,
+                                                         float* __restrict__ sigma, ScoreP P) {
+#pragma clang fp contract(off)
+    extern __shared__ float lds[];
+    const int64_t bh = blockIdx.y;
+    const int64_t c0 = (int64_t)blockIdx.x * P.chunk;
+    const int len = (int)((P.N - c0) < P.chunk ? (P.N - c0) : P.chunk);
+    const int cw = (int)(P.d / 8);
+    const int r = threadIdx.x & 7;
+    for (int tok = threadIdx.x >> 3; tok < len; tok += kThreads / 8) {
+        const int64_t row = (bh * P.N + c0 + tok) * P.d + r * cw;
+        const float sq = tree8(sumsq_lane(q + row, cw));
+        const float sk = tree8(sumsq_lane(k + row, cw));
+        if (r == 0) lds[tok] = sqrtf(sq) + sqrtf(sk);
+    }
+    __syncthreads();
+    int prev_off = 0, cur_off = len;
+    int n_prev = len;
+    float* sg = sigma + bh * P.Mu;
+    for (int l = 1; l < P.L; ++l) {
+        const int n = n_prev / P.p;
+        const int64_t e0 = c0 / P.pw[l];
+        for (int e = threadIdx.x; e < n; e += kThreads) {
+            float m = lds[prev_off + e * P.p];
+            for (int c = 1; c < P.p; ++c) m = fmaxf(m, lds[prev_off + e * P.p + c]);
+            lds[cur_off + e] = m;
+            sg[P.offu[l] + e0 + e] = m;
+        }
+        __syncthreads();
+        prev_off = cur_off;
+        cur_off += n;
+        n_prev = n;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Exact top-K of one level of one head: one block of 1024 threads.
+// Scores are non-negative floats, so their bit patterns order like the
+// values.  An MSB-first radix select (12, 12 and 8 bits) finds the k-th
+// largest value tau and how many entries equal to tau must be taken; those
+// are the lowest-index ones (ties go to the lower index).  The result is a
+// bitmap of the level plus the exclusive popcount prefix of each word.
+// ---------------------------------------------------------------------------
+struct TopkP {
+    int64_t BH, Mu, words_total;
+    int L;
+    int64_t M[LH_MAX_LEVELS], k_eff[LH_MAX_LEVELS], offu[LH_MAX_LEVELS], woff[LH_MAX_LEVELS];
+};
+
+constexpr int kTopkThreads = 1024;
+
+// Exclusive scan over the 1024 threads of a block; *total = sum of all.
+__device__ uint32_t block_excl_scan(uint32_t v, uint32_t* wsum, uint32_t* total) {
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    uint32_t x = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t y = __shfl_up(x, o, 64);
+        if (lane >= o) x += y;
+    }
+    if (lane == 63) wsum[wid] = x;
+    __syncthreads();
+    if (wid == 0) {
+        uint32_t t = lane < 16 ? wsum[lane] : 0u;
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) {
+            const uint32_t y = __shfl_up(t, o, 64);
+            if (lane >= o) t += y;
+        }
+        if (lane < 16) wsum[16 + lane] = t;
+    }
+    __syncthreads();
+    const uint32_t base = wid > 0 ? wsum[16 + wid - 1] : 0u;
+    *total = wsum[31];
+    const uint32_t res = base + x - v;
+    __syncthreads();
+    return res;
+}
+
+__global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restrict__ sigma,
+                                                            uint32_t* __restrict__ words,
+                                                            int32_t* __restrict__ prefix, TopkP P) {
+    __shared__ uint32_t hist[4096];
+    __shared__ uint32_t wsum[32];
+    __shared__ uint32_t s_bin, s_above;
+    const int l = blockIdx.x + 1;
+    const int64_t bh = blockIdx.y;
+    const int64_t M = P.M[l];
+    const uint32_t kk = (uint32_t)P.k_eff[l];
+    const uint32_t* sg = reinterpret_cast<const uint32_t*>(sigma + bh * P.Mu + P.offu[l]);
+    uint32_t* W = words + bh * P.words_total + P.woff[l];
+    int32_t* PC = prefix + bh * P.words_total + P.woff[l];
+    const int64_t nw = (M + 31) / 32;
+    const int tid = threadIdx.x;
+    const bool all = (int64_t)kk >= M;
+
+    uint32_t tau = 0, take = 0;
+    if (!all) {
+        uint32_t pre = 0, pmask = 0, remaining = kk;
+        for (int pass = 0; pass < 3; ++pass) {
+            const int shift = pass == 0 ? 20 : (pass == 1 ? 8 : 0);
+            const uint32_t dmask = pass == 2 ? 0xFFu : 0xFFFu;
+            for (int b = tid; b < 4096; b += kTopkThreads) hist[b] = 0;
+            __syncthreads();
+            for (int64_t i = tid; i < M; i += kTopkThreads) {
+                const uint32_t u = sg[i];
+                if ((u & pmask) == pre) atomicAdd(&hist[(u >> shift) & dmask], 1u);
+            }
+            __syncthreads();
+            const int g = kTopkThreads - 1 - tid;     // descending bins
+            uint32_t hb[4];
+            uint32_t gs = 0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                hb[j] = hist[4 * g + j];
+                gs += hb[j];
+            }
+            uint32_t tot;
+            uint32_t above = block_excl_scan(gs, wsum, &tot);
+#pragma unroll
+            for (int j = 3; j >= 0; --j) {
+                if (above < remaining && remaining <= above + hb[j]) {
+                    s_bin = 4 * g + j;
+                    s_above = above;
+                }
+                above += hb[j];
+            }
+            __syncthreads();
+            const uint32_t b = s_bin;
+            remaining -= s_above;
+            pre |= b << shift;
+            pmask |= dmask << shift;
+            __syncthreads();
+        }
+        tau = pre;
+        take = remaining;
+    }
+
+    uint32_t carry_tie = 0, carry_pc = 0;
+    for (int64_t w0 = 0; w0 < nw; w0 += kTopkThreads) {
+        const int64_t w = w0 + tid;
+        uint32_t gt = 0, eq = 0;
+        if (w < nw) {
+            for (int b = 0; b < 32; ++b) {
+                const int64_t i = w * 32 + b;
+                if (i < M) {
+                    const uint32_t u = sg[i];
+                    if (all || u > tau) gt |= 1u << b;
+                    else if (u == tau) eq |= 1u << b;
+                }
+            }
+        }
+        uint32_t tot;
+        const uint32_t ex = block_excl_scan((uint32_t)__popc(eq), wsum, &tot);
+        uint32_t sel = gt;
+        const uint32_t base = carry_tie + ex;
+        if (take > base) {
+            uint32_t want = take - base, e = eq;
+            while (want && e) {
+                const uint32_t low = e & (0u - e);
+                sel |= low;
+                e ^= low;
+                --want;
+            }
+        }
+        carry_tie += tot;
+        uint32_t tot2;
+        const uint32_t ex2 = block_excl_scan((uint32_t)__popc(sel), wsum, &tot2);
+        if (w < nw) {
+            W[w] = sel;
+            PC[w] = (int32_t)(carry_pc + ex2);
+        }
+        carry_pc += tot2;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Gather map: each pyramid entry finds whether it is selected and, if so, its
+// slot = number of selected entries ordered before it by (span end, level).
+// With P_l[x] = selected level-l entries among [0, x):
+//   slot(l, i) = P_l[i] + sum_{l'<l} P_l'[(i+1) p^(l-l')]
+//                       + sum_{l'>l} P_l'[ceil((i+1)/p^(l'-l)) - 1].
+// Level l-1 entries are selected exactly when their parent is in T_l, so
+// P_{l-1}[x] = p * #T_l[0, x/p) + (x mod p) * [x/p in T_l]; the coarsest
+// level is whole, P_{L-1}[x] = x.
+// ---------------------------------------------------------------------------
+struct MapP {
+    int64_t BH, M_total, S, words_total;
+    int p, L;
+    int64_t M[LH_MAX_LEVELS], k_eff[LH_MAX_LEVELS], off[LH_MAX_LEVELS + 1], pw[LH_MAX_LEVELS],
+        woff[LH_MAX_LEVELS];
+};
+
+__device__ __forceinline__ bool t_bit(const uint32_t* W, int64_t y) { return (W[y >> 5] >> (y & 31)) & 1u; }
+
+__device__ __forceinline__ int64_t sel_before(const MapP& P, const uint32_t* Wh, const int32_t* PCh, int lp,
+                                              int64_t x) {
+    if (lp == P.L - 1) return x;
+    const int64_t y = x / P.p, r = x - y * P.p;
+    const uint32_t* W = Wh + P.woff[lp + 1];
+    const int32_t* PC = PCh + P.woff[lp + 1];
+    const int64_t Mn = P.M[lp + 1];
+    int64_t c;
+    if (y >= Mn) {
+        c = P.k_eff[lp + 1];
+    } else {
+        const uint32_t m = (1u << (y & 31)) - 1u;
+        c = PC[y >> 5] + __popc(W[y >> 5] & m);
+    }
+    c *= P.p;
+    if (r && y < Mn && t_bit(W, y)) c += r;
+    return c;
+}
+
+__global__ __launch_bounds__(kThreads) void map_kernel(const uint32_t* __restrict__ words,
+                                                       const int32_t* __restrict__ prefix,
+                                                       int32_t* __restrict__ gidx, int32_t* __restrict__ gpos,
+                                                       MapP P) {
+    const int64_t id = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    const int64_t bh = blockIdx.y;
+    if (id >= P.M_total) return;
+    int l = 0;
+    while (id >= P.off[l + 1]) ++l;
+    const int64_t i = id - P.off[l];
+    const uint32_t* Wh = words + bh * P.words_total;
+    const int32_t* PCh = prefix + bh * P.words_total;
+    const bool sel = (l == P.L - 1) || t_bit(Wh + P.woff[l + 1], i / P.p);
+    if (!sel) {
+        gpos[bh * P.M_total + id] = -1;
+        return;
+    }
+    int64_t pos = sel_before(P, Wh, PCh, l, i);
+    for (int lp = 0; lp < l; ++lp) pos += sel_before(P, Wh, PCh, lp, (i + 1) * P.pw[l - lp]);
+    for (int lp = l + 1; lp < P.L; ++lp) {
+        const int64_t n = P.pw[lp - l];
+        pos += sel_before(P, Wh, PCh, lp, (i + n) / n - 1);
+    }
+    if (pos < 0 || pos >= P.S) pos = -1;   // unreachable for a consistent bitmap; never write out of range
+    gpos[bh * P.M_total + id] = (int32_t)pos;
+    if (pos >= 0) gidx[bh * P.S + pos] = (int32_t)id;
+}
+
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+hipError_t launch_pool(const LhGeom& g, int dtype, const void* q, const void* k, const void* v, void* pyr,
+                       hipStream_t st) {
+    if (g.L < 2) return hipSuccess;
+    PoolP P{};
+    P.N = g.N; P.d = g.d; P.BH = g.BH; P.Mu = g.Mu; P.p = g.p; P.L = g.L;
+    for (int l = 0; l < g.L; ++l) { P.offu[l] = l ? g.off[l] - g.N : 0; P.pw[l] = g.pw[l]; }
+    const int VEC = dtype == LH_BF16 ? 8 : 4;
+    int64_t chunk = g.pw[g.L - 1];
+    while (chunk < 256 && chunk * 2 <= g.N) chunk *= 2;
+    // chunk must stay a multiple of p^(L-1): it is p^(L-1) * 2^j
+    int DS = (int)g.d;
+    auto lds_bytes = [&](int64_t ch, int ds) {
+        int64_t ent = 0;
+        for (int l = 1; l < g.L; ++l) ent += ch / g.pw[l];
+        return ent * ds * 4;
+    };
+    while (lds_bytes(chunk, DS) > 48 * 1024 && chunk > g.pw[g.L - 1]) chunk /= 2;
+    while (lds_bytes(chunk, DS) > 48 * 1024 && DS > VEC) DS /= 2;
+    if (lds_bytes(chunk, DS) > 64 * 1024) return hipErrorInvalidValue;
+    P.chunk = (int)chunk; P.DS = DS; P.nslices = (int)(g.d / DS);
+    dim3 grid((unsigned)(ceil_div(g.N, chunk) * P.nslices), (unsigned)g.BH, 3);
+    size_t sh = (size_t)lds_bytes(chunk, DS);
+    if (dtype == LH_BF16)
+        pool_kernel<bf16><<<grid, kThreads, sh, st>>>((const bf16*)q, (const bf16*)k, (const bf16*)v, (bf16*)pyr, P);
+    else
+        pool_kernel<float><<<grid, kThreads, sh, st>>>((const float*)q, (const float*)k, (const float*)v, (float*)pyr, P);
+    return hipGetLastError();
+}
+
+hipError_t launch_scores(const LhGeom& g, int dtype, const void* q, const void* k, float* sigma, hipStream_t st) {
+    if (g.L < 2) return hipSuccess;
+    ScoreP P{};
+    P.N = g.N; P.d = g.d; P.BH = g.BH; P.Mu = g.Mu; P.p = g.p; P.L = g.L;
+    for (int l = 0; l < g.L; ++l) { P.offu[l] = l ? g.off[l] - g.N : 0; P.pw[l] = g.pw[l]; }
+    int64_t chunk = g.pw[g.L - 1];
+    while (chunk < 1024 && chunk * 2 <= g.N) chunk *= 2;
+    if (chunk > 16384) return hipErrorInvalidValue;
+    P.chunk = (int)chunk;
+    int64_t ent = chunk;
+    for (int l = 1; l < g.L; ++l) ent += chunk / g.pw[l];
+    dim3 grid((unsigned)ceil_div(g.N, chunk), (unsigned)g.BH);
+    if (dtype == LH_BF16)
+        score_kernel<bf16><<<grid, kThreads, ent * 4, st>>>((const bf16*)q, (const bf16*)k, sigma, P);
+    else
+        score_kernel<float><<<grid, kThreads, ent * 4, st>>>((const float*)q, (const float*)k, sigma, P);
+    return hipGetLastError();
+}
+
+hipError_t launch_topk(const LhGeom& g, const float* sigma, uint32_t* words, int32_t* prefix, hipStream_t st) {
+    if (g.L < 2) return hipSuccess;
+    TopkP P{};
+    P.BH = g.BH; P.Mu = g.Mu; P.words_total = g.words_total; P.L = g.L;
+    for (int l = 0; l < g.L; ++l) {
+        P.M[l] = g.M[l]; P.k_eff[l] = g.k_eff[l];
+        P.offu[l] = l ? g.off[l] - g.N : 0;
+        P.woff[l] = g.words_off[l];
+    }
+    dim3 grid((unsigned)(g.L - 1), (unsigned)g.BH);
+    topk_kernel<<<grid, kTopkThreads, 0, st>>>(sigma, words, prefix, P);
+    return hipGetLastError();
+}
+
+hipError_t launch_map(const LhGeom& g, const uint32_t* words, const int32_t* prefix, int32_t* gidx, int32_t* gpos,
+                      hipStream_t st) {
+    MapP P{};
+    P.BH = g.BH; P.M_total = g.M_total; P.S = g.S; P.words_total = g.words_total; P.p = g.p; P.L = g.L;
+    for (int l = 0; l < g.L; ++l) {
+        P.M[l] = g.M[l]; P.k_eff[l] = g.k_eff[l]; P.pw[l] = g.pw[l]; P.woff[l] = g.words_off[l];
+    }
+    for (int l = 0; l <= g.L; ++l) P.off[l] = g.off[l];
+    dim3 grid((unsigned)ceil_div(g.M_total, kThreads), (unsigned)g.BH);
+    map_kernel<<<grid, kThreads, 0, st>>>(words, prefix, gidx, gpos, P);
+    return hipGetLastError();
+}

@@ -19,10 +19,12 @@ Precision.  Everything is float64 except the token scores, which are float32
 in one fixed order so that the integer decisions built on them (the selected
 sets and the gather order) are reproducible bit for bit by any
 implementation that follows the same order.  Where a tensor of the layer's
-dtype is stored (pyramid levels >= 1, the sub-sequence output, its gradient
-and the final outputs/gradients) the oracle rounds to that dtype once, with
-round-to-nearest-even, exactly as a bf16/fp32 implementation stores it; the
-"f64" dtype turns every such rounding off (used by finite differences).
+dtype is stored and reused (pyramid levels >= 1, the gradient of the
+sub-sequence output, which feeds matrix products, and the final outputs and
+gradients) the oracle rounds to that dtype once, with round-to-nearest-even,
+exactly as a bf16/fp32 implementation stores it; the sub-sequence output
+itself is an intermediate and stays unrounded.  The "f64" dtype turns every
+rounding off (used by finite differences).
 
 Readings of points the pages leave open (each is used below and listed with
 its reasons in the design notes):
@@ -378,8 +380,7 @@ def head_forward(q, k, v, p, L, kk, dtype, scale=None, selection=None):
         gidx, gpos = selection
     lq, lk, lv = pyramid(q, p, L, dtype), pyramid(k, p, L, dtype), pyramid(v, p, L, dtype)
     Qt, Kt, Vt = gather(lq, gidx, plan), gather(lk, gidx, plan), gather(lv, gidx, plan)
-    Ot_raw, lse = attention_forward(Qt, Kt, Vt, scale)
-    Ot = round_to(Ot_raw, dtype)
+    Ot, lse = attention_forward(Qt, Kt, Vt, scale)
     O = round_to(scatter(Ot, gpos, plan), dtype)
     return dict(plan=plan, scale=scale, gidx=gidx, gpos=gpos, levels=(lq, lk, lv),
                 Qt=Qt, Kt=Kt, Vt=Vt, Ot=Ot, lse=lse, O=O, dtype=dtype)

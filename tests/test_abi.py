@@ -1,0 +1,107 @@
+"""The C ABI on the CPU: the library loads, exports what the header declares,
+sizes problems like the oracle, and rejects bad arguments before launching
+anything (no GPU needed: every check here fails before a launch)."""
+import ctypes
+
+import pytest
+
+from long_context_pretraining_amd import lighthouse as lh
+from oracle import lighthouse_oracle as orc
+from tests.conftest import read_golden
+
+FAKE = 0x100000          # aligned, never dereferenced: every call below fails validation first
+
+
+def test_exports_every_header_function():
+    lib = lh.load_library()
+    names = lh.header_functions()
+    assert set(names) == {"lh_make_plan", "lh_pyramid", "lh_score_topk", "lh_forward", "lh_backward",
+                          "dense_causal_attn", "dense_causal_attn_backward", "lh_status_string"}
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings():
+    for s in (lh.LH_OK, lh.LH_E_ARG, lh.LH_E_UNSUPPORTED, lh.LH_E_WORKSPACE, lh.LH_E_DEVICE, 17):
+        assert isinstance(lh.status_string(s), str) and lh.status_string(s)
+
+
+@pytest.mark.parametrize("N,p,L,k,d,dt", [(4096, 4, 3, 64, 64, 0), (98304, 4, 4, 1536, 64, 1), (98304, 4, 4, 6144, 64, 1),
+                                          (524288, 4, 6, 1536, 64, 1), (1000, 2, 3, 13, 128, 1), (729, 3, 4, 7, 64, 1),
+                                          (256, 4, 1, 1, 64, 0)])
+def test_plan_matches_oracle(N, p, L, k, d, dt):
+    plan = lh.lh_make_plan(lh.make_desc(1, 2, N, d, p, L, k, dt))
+    ref = orc.make_plan(N, p, L, k)
+    assert list(plan.M)[:L] == ref.M
+    assert list(plan.k_eff)[1:L] == ref.k_eff[1:]
+    assert list(plan.level_off)[:L + 1] == ref.level_off
+    assert plan.M_total == ref.M_total and plan.S == ref.S and plan.S_formula == ref.S_formula
+    assert plan.S_pad % 64 == 0 and plan.S <= plan.S_pad < plan.S + 64
+    e = 4 if dt == 0 else 2
+    assert plan.pyr_bytes == 3 * 2 * (ref.M_total - N) * d * e
+    offs = list(plan.fwd_off)
+    assert offs == sorted(offs) and all(o % 256 == 0 for o in offs) and plan.fwd_ws_bytes > offs[-1]
+
+
+def test_plan_golden_s():
+    for N, p, L, k, Sf, Sa in read_golden("s_formula.txt"):
+        plan = lh.lh_make_plan(lh.make_desc(1, 1, int(N), 64, int(p), int(L), int(k), 1))
+        assert (plan.S_formula, plan.S) == (int(Sf), int(Sa))
+
+
+@pytest.mark.parametrize("args,code", [
+    ((1, 1, 100, 64, 4, 3, 1, 1), lh.LH_E_ARG),        # N not a multiple of p^(L-1)
+    ((1, 1, 64, 64, 1, 2, 1, 1), lh.LH_E_ARG),         # p < 2
+    ((1, 1, 64, 64, 2, 0, 1, 1), lh.LH_E_ARG),         # L < 1
+    ((1, 1, 64, 64, 2, 9, 1, 1), lh.LH_E_ARG),         # L > 8
+    ((1, 1, 64, 64, 2, 2, 0, 1), lh.LH_E_ARG),         # k < 1
+    ((0, 1, 64, 64, 2, 2, 1, 1), lh.LH_E_ARG),         # B < 1
+    ((1, 1, 64, 64, 2, 2, 1, 7), lh.LH_E_ARG),         # unknown dtype
+    ((1, 1, 64, 60, 2, 2, 1, 1), lh.LH_E_ARG),         # d not a multiple of 8
+    ((1, 1, 64, 96, 2, 2, 1, 1), lh.LH_E_UNSUPPORTED), # d = 96 not built
+    ((1, 1, 64, 128, 2, 2, 1, 0), lh.LH_E_UNSUPPORTED),  # f32 with d = 128 not built
+    ((1, 1, 8, 64, 4, 3, 1, 1), lh.LH_E_ARG),          # p^(L-1) > N
+])
+def test_plan_rejects(args, code):
+    with pytest.raises(lh.LighthouseError) as e:
+        lh.lh_make_plan(lh.make_desc(*args))
+    assert e.value.status == code
+
+
+def _call(name, *args):
+    lib = lh.load_library()
+    return getattr(lib, name)(*args)
+
+
+def test_entry_points_validate_before_launch():
+    desc = lh.make_desc(1, 2, 4096, 64, 4, 3, 64, 1)
+    plan = lh.lh_make_plan(desc)
+    D = ctypes.byref(desc)
+    # null pointers
+    assert _call("lh_pyramid", D, None, FAKE, FAKE, FAKE, plan.pyr_bytes, None) == lh.LH_E_ARG
+    assert _call("lh_score_topk", D, FAKE, FAKE, None, FAKE, FAKE, plan.sel_ws_bytes, None) == lh.LH_E_ARG
+    assert _call("lh_forward", D, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, plan.fwd_ws_bytes, None) == lh.LH_E_ARG
+    assert _call("lh_backward", D, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, plan.bwd_ws_bytes, None) == lh.LH_E_ARG
+    # misaligned pointers
+    assert _call("lh_pyramid", D, FAKE + 2, FAKE, FAKE, FAKE, plan.pyr_bytes, None) == lh.LH_E_ARG
+    assert _call("dense_causal_attn", D, FAKE, FAKE, FAKE, FAKE, FAKE + 4, FAKE, plan.dense_fwd_ws_bytes, None) == lh.LH_E_ARG
+    # short workspaces
+    assert _call("lh_pyramid", D, FAKE, FAKE, FAKE, FAKE, plan.pyr_bytes - 1, None) == lh.LH_E_WORKSPACE
+    assert _call("lh_score_topk", D, FAKE, FAKE, FAKE, FAKE, FAKE, plan.sel_ws_bytes - 1, None) == lh.LH_E_WORKSPACE
+    assert _call("lh_forward", D, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, plan.fwd_ws_bytes - 1, None) == lh.LH_E_WORKSPACE
+    assert _call("lh_backward", D, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, plan.bwd_ws_bytes - 1, None) == lh.LH_E_WORKSPACE
+    assert _call("dense_causal_attn", D, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, plan.dense_fwd_ws_bytes - 1, None) == lh.LH_E_WORKSPACE
+    assert _call("dense_causal_attn_backward", D, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                 plan.dense_bwd_ws_bytes - 1, None) == lh.LH_E_WORKSPACE
+    # bad descriptor
+    bad = lh.make_desc(1, 2, 4095, 64, 4, 3, 64, 1)
+    assert _call("lh_forward", ctypes.byref(bad), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40, None) == lh.LH_E_ARG
+    assert _call("lh_make_plan", None, None) == lh.LH_E_ARG
+
+
+def test_tensor_marshalling_rejects_host_tensors():
+    import torch
+    desc = lh.make_desc(1, 1, 64, 64, 2, 2, 1, 1)
+    t = torch.zeros(10)
+    with pytest.raises(ValueError):
+        lh.lh_pyramid(desc, t, t, t, t)
