@@ -1,0 +1,242 @@
+#!/usr/bin/env python3
+"""Lighthouse Attention layer, forward + backward, on one MI355X.
+
+One step = lh_pyramid + lh_score_topk + lh_forward + lh_backward over the
+whole layer (all heads) on seeded synthetic inputs already resident in HBM;
+selection is recomputed every step, as in training.  The workload is the
+530M Llama-3-style attention layer at 98,304 tokens with k = 1536
+(B=1, H=16, N=98304, d=64, bf16, p=4, L=4; S = 19968).
+
+Prints ONE JSON line: tokens/s of the layer (B*N per step), the dense causal
+attention baseline on the same GPU and inputs (speedup), the roofline of the
+dominant kernel measured live with HIP events on the library's stream, and
+the CPU oracle timed on a bounded sample.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFS = 2500.0    # dense bf16 matrix cores
+MFMA_F32_PEAK_TFS = 157.3
+
+KERNEL_NAMES = ["pool", "score", "topk", "map", "gather", "attn_fwd", "scatter_fwd", "scatter_bwd",
+                "attn_dkdv", "attn_dq", "gather_pool_bwd"]
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="llama530m_98k_k1536")
+    ap.add_argument("--dense-steps", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+class HipEvents:
+    """Raw hipEvent_t handles (the probe hook records them on the library's stream)."""
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+
+    def create(self):
+        ev = ctypes.c_void_p()
+        assert self.hip.hipEventCreate(ctypes.byref(ev)) == 0
+        return ev
+
+    def elapsed_ms(self, a, b):
+        self.hip.hipEventSynchronize(b)
+        ms = ctypes.c_float()
+        assert self.hip.hipEventElapsedTime(ctypes.byref(ms), a, b) == 0
+        return ms.value
+
+    def destroy(self, ev):
+        self.hip.hipEventDestroy(ev)
+
+
+def algorithmic_work(name, w, plan):
+    """(bound, work per launch, unit) -- flops for the attention kernels
+    (causal half: S(S+1)/2 score pairs per head, 2d flops per pair per
+    product), bytes the method must move for the others."""
+    BH, N, d, S = w.B * w.H, w.N, w.d, plan.S
+    e = 2 if w.dtype == "bf16" else 4
+    pairs = S * (S + 1) / 2
+    Mu = plan.M_total - N
+    if name == "attn_fwd":          # Q K^T and P V
+        return "mfma", BH * 2 * 2 * d * pairs, "flop"
+    if name == "attn_dkdv":         # recompute Q K^T, dO V^T, P^T dO, dS^T Q
+        return "mfma", BH * 4 * 2 * d * pairs, "flop"
+    if name == "attn_dq":           # dS K (the recomputed products are not counted)
+        return "mfma", BH * 1 * 2 * d * pairs, "flop"
+    table = {
+        "pool": 3 * N * d * e + 3 * Mu * d * e,
+        "score": 2 * N * d * e + Mu * 4,
+        "gather": 2 * 3 * S * d * e + S * 4,
+        "scatter_fwd": S * d * 4 + N * d * e + plan.M_total * 4,
+        "scatter_bwd": N * d * e + S * d * e + S * d * 4 + S * 4,
+        "gather_pool_bwd": 3 * S * d * 4 + 3 * N * d * e + plan.M_total * 4,
+        "topk": Mu * 4,
+        "map": plan.M_total * 4 + S * 4,
+    }
+    return "hbm", BH * table[name], "byte"
+
+
+def cpu_baseline(w, q, k, v, dout, nheads=6):
+    """The oracle as it stands on the first `nheads` heads of the workload:
+    selection, pyramid, attention, scatter and the whole backward, per head;
+    scaled to the layer."""
+    import numpy as np
+    from oracle import lighthouse_oracle as orc
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        cores = 1
+    heads = w.B * w.H
+    nheads = min(nheads, heads)
+    dt = 0.0
+    for h in range(nheads):
+        qh, kh, vh, gh = (x[0, h].float().numpy().astype(np.float64) for x in (q, k, v, dout))
+        t0 = time.perf_counter()
+        st = orc.head_forward(qh, kh, vh, w.p, w.L, w.k, w.dtype)
+        orc.head_backward(st, gh)
+        dt += time.perf_counter() - t0
+    per_head = dt / nheads
+    return {"value": round(w.B * w.N / (per_head * heads), 1), "unit": "tokens/s", "cores": int(cores),
+            "kind": "oracle",
+            "sample": f"{nheads} of {heads} heads (b=0, h<{nheads}), full fwd+bwd incl. selection, {dt:.1f} s "
+                      f"of CPU time; value = B*N / (mean time per head x {heads} heads)"}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py runs on exactly one GPU: the layer is measured per GPU and this build has no "
+              "multi-GPU path (heads shard across GPUs with no communication; see the design notes).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from long_context_pretraining_amd import inputs
+    from long_context_pretraining_amd import lighthouse as lh
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    lh.load_library()
+    w = inputs.WORKLOADS[args.workload]
+    dt = inputs.TORCH_DTYPE[w.dtype]
+    q, k, v = inputs.make_qkv(w)
+    dout = inputs.make_dout(w)
+    dev = torch.device("cuda:0")
+    qd, kd, vd, dod = (x.to(dev) for x in (q, k, v, dout))
+    layer = lh.LighthouseLayer(w.B, w.H, w.N, w.d, w.p, w.L, w.k, dt)
+    plan = layer.plan
+    o, dq, dk, dv = (torch.empty_like(qd) for _ in range(4))
+
+    def step():
+        layer.forward(qd, kd, vd, o)
+        layer.backward(dod, dq, dk, dv)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # per-kernel durations (one probed step each) to find the dominant kernel
+    ev = HipEvents()
+    a, b = ev.create(), ev.create()
+    kernel_ms = {}
+    for kid, name in enumerate(KERNEL_NAMES):
+        lh.lh_set_probe(kid, a, b)
+        step()
+        torch.cuda.synchronize()
+        kernel_ms[name] = ev.elapsed_ms(a, b)
+    lh.lh_set_probe(-1, None, None)
+    dominant = max(kernel_ms, key=kernel_ms.get)
+    dom_id = KERNEL_NAMES.index(dominant)
+
+    # timed region: exactly K steps, the dominant kernel probed in every step
+    starts = [ev.create() for _ in range(args.steps)]
+    stops = [ev.create() for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        lh.lh_set_probe(dom_id, starts[i], stops[i])
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    lh.lh_set_probe(-1, None, None)
+    elapsed = t1 - t0
+    ms_step = elapsed * 1e3 / args.steps
+    dom_ms = sum(ev.elapsed_ms(s, e) for s, e in zip(starts, stops)) / args.steps
+    tokens_per_s = w.B * w.N * args.steps / elapsed
+
+    bound, work, unit = algorithmic_work(dominant, w, plan)
+    if bound == "mfma":
+        peak = MFMA_BF16_PEAK_TFS if w.dtype == "bf16" else MFMA_F32_PEAK_TFS
+        achieved = work / (dom_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(achieved / peak, 4), "traffic": None, "kernel": dominant,
+                "kernel_ms": round(dom_ms, 4), "work_per_launch": work}
+    else:
+        achieved = work / (dom_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None, "kernel": dominant,
+                "kernel_ms": round(dom_ms, 4), "work_per_launch": work}
+
+    # dense causal attention baseline on the same GPU and inputs
+    ddesc = lh.make_desc(w.B, w.H, w.N, w.d, w.p, 1, 1, dt)
+    dplan = lh.lh_make_plan(ddesc)
+    dws = torch.empty(dplan.dense_fwd_ws_bytes, dtype=torch.uint8, device=dev)
+    dwsb = torch.empty(dplan.dense_bwd_ws_bytes, dtype=torch.uint8, device=dev)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+
+    def dense_step():
+        lh.dense_causal_attn(ddesc, qd, kd, vd, o, lse, dws)
+        lh.dense_causal_attn_backward(ddesc, qd, kd, vd, lse, dws, dod, dq, dk, dv, dwsb)
+
+    dense_step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.dense_steps):
+        dense_step()
+    torch.cuda.synchronize()
+    dense_ms = (time.perf_counter() - t0) * 1e3 / args.dense_steps
+    del dws, dwsb
+
+    out = {
+        "metric": "Lighthouse fwd+bwd tokens/s at N=98K,k=1536; speedup vs dense causal attn",
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "p": w.p, "L": w.L, "k": w.k,
+                   "S": plan.S, "S_formula": plan.S_formula},
+        "speedup_vs_dense": round(dense_ms / ms_step, 3),
+        "dense_ms_per_step": round(dense_ms, 3),
+        "dense_tokens_per_s": round(w.B * w.N / (dense_ms * 1e-3), 1),
+        "kernel_ms": {n: round(x, 4) for n, x in kernel_ms.items()},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, q, k, v, dout)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

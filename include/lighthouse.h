@@ -178,6 +178,21 @@ lh_status dense_causal_attn_backward(const lh_desc* desc, const void* q, const v
 /* Static string for a status code. */
 const char* lh_status_string(int status);
 
+/* Measurement hook (for benchmarks, not for the data path).  After
+ * lh_set_probe(kernel, start, stop), every later call that launches kernel
+ * `kernel` records hipEvent_t `start` on its stream just before that launch
+ * and `stop` just after it, so hipEventElapsedTime(start, stop) is the
+ * kernel's duration as the stream sees it.  kernel = -1 (or null events)
+ * switches the hook off.  The setting is process-wide and not thread-safe;
+ * the events are owned by the caller. */
+enum {
+    LH_KERNEL_POOL = 0, LH_KERNEL_SCORE, LH_KERNEL_TOPK, LH_KERNEL_MAP, LH_KERNEL_GATHER,
+    LH_KERNEL_ATTN_FWD, LH_KERNEL_SCATTER_FWD, LH_KERNEL_SCATTER_BWD, LH_KERNEL_ATTN_DKDV,
+    LH_KERNEL_ATTN_DQ, LH_KERNEL_GATHER_POOL_BWD, LH_KERNEL_TRANSPOSE, LH_KERNEL_DENSE_PREP,
+    LH_KERNEL_COUNT
+};
+lh_status lh_set_probe(int kernel, void* start_event, void* stop_event);
+
 #ifdef __cplusplus
 }
 #endif

@@ -95,6 +95,19 @@ inline const unsigned char* at(const void* base, size_t off) { return static_cas
 
 float softmax_scale(const lh_desc* d) { return d->scale > 0.f ? d->scale : 1.0f / sqrtf((float)d->d); }
 
+// Measurement hook (lh_set_probe): events recorded around one kernel's launches.
+int g_probe_kernel = -1;
+hipEvent_t g_probe_start = nullptr, g_probe_stop = nullptr;
+
+template <class F>
+hipError_t probed(int id, hipStream_t st, F&& launch) {
+    const bool on = id == g_probe_kernel && g_probe_start && g_probe_stop;
+    if (on) hipEventRecord(g_probe_start, st);
+    const hipError_t e = launch();
+    if (on) hipEventRecord(g_probe_stop, st);
+    return e;
+}
+
 }  // namespace
 
 extern "C" {
@@ -122,7 +135,8 @@ lh_status lh_pyramid(const lh_desc* desc, const void* q, const void* k, const vo
     if (P.pyr_bytes == 0) return LH_OK;
     if (!aligned(pyr)) return LH_E_ARG;
     if (pyr_bytes < P.pyr_bytes) return LH_E_WORKSPACE;
-    return dev(launch_pool(g, desc->dtype, q, k, v, pyr, (hipStream_t)stream));
+    hipStream_t st = (hipStream_t)stream;
+    return dev(probed(LH_KERNEL_POOL, st, [&] { return launch_pool(g, desc->dtype, q, k, v, pyr, st); }));
 }
 
 lh_status lh_score_topk(const lh_desc* desc, const void* q, const void* k, int32_t* gidx, int32_t* gpos, void* ws,
@@ -139,9 +153,10 @@ lh_status lh_score_topk(const lh_desc* desc, const void* q, const void* k, int32
     const size_t sz_sigma = align_up((size_t)g.BH * g.Mu * 4), sz_w = align_up((size_t)g.BH * g.words_total * 4);
     uint32_t* words = (uint32_t*)at(ws, sz_sigma);
     int32_t* prefix = (int32_t*)at(ws, sz_sigma + sz_w);
-    hipError_t e = launch_scores(g, desc->dtype, q, k, sigma, st);
-    if (e == hipSuccess) e = launch_topk(g, sigma, words, prefix, st);
-    if (e == hipSuccess) e = launch_map(g, words, prefix, gidx, gpos, st);
+    hipError_t e = probed(LH_KERNEL_SCORE, st, [&] { return launch_scores(g, desc->dtype, q, k, sigma, st); });
+    if (e == hipSuccess) e = probed(LH_KERNEL_TOPK, st, [&] { return launch_topk(g, sigma, words, prefix, st); });
+    if (e == hipSuccess)
+        e = probed(LH_KERNEL_MAP, st, [&] { return launch_map(g, words, prefix, gidx, gpos, st); });
     return dev(e);
 }
 
@@ -162,12 +177,16 @@ lh_status lh_forward(const lh_desc* desc, const void* q, const void* k, const vo
     void* cols[3] = {at(fwd_ws, P.fwd_off[LH_FWD_QT]), at(fwd_ws, P.fwd_off[LH_FWD_KT]), at(fwd_ws, P.fwd_off[LH_FWD_VT])};
     float* og = (float*)at(fwd_ws, P.fwd_off[LH_FWD_O]);
     float* lse = (float*)at(fwd_ws, P.fwd_off[LH_FWD_LSE]);
-    hipError_t e = launch_gather(g, desc->dtype, q, k, v, pyr, gidx, rows, cols, st);
+    hipError_t e = probed(LH_KERNEL_GATHER, st,
+                          [&] { return launch_gather(g, desc->dtype, q, k, v, pyr, gidx, rows, cols, st); });
     if (e == hipSuccess) {
         AttnArgs a{g.BH, g.S, g.S_pad, g.d, softmax_scale(desc)};
-        e = launch_attn_fwd(a, desc->dtype, rows[0], rows[1], cols[2], og, nullptr, lse, st);
+        e = probed(LH_KERNEL_ATTN_FWD, st, [&] {
+            return launch_attn_fwd(a, desc->dtype, rows[0], rows[1], cols[2], og, nullptr, lse, st);
+        });
     }
-    if (e == hipSuccess) e = launch_scatter_fwd(g, desc->dtype, og, gpos, o, st);
+    if (e == hipSuccess)
+        e = probed(LH_KERNEL_SCATTER_FWD, st, [&] { return launch_scatter_fwd(g, desc->dtype, og, gpos, o, st); });
     return dev(e);
 }
 
@@ -190,17 +209,28 @@ lh_status lh_backward(const lh_desc* desc, const int32_t* gidx, const int32_t* g
     float* Dv = (float*)at(bwd_ws, P.bwd_off[LH_BWD_D]);
     float* dxg[3] = {(float*)at(bwd_ws, P.bwd_off[LH_BWD_DQ]), (float*)at(bwd_ws, P.bwd_off[LH_BWD_DK]),
                      (float*)at(bwd_ws, P.bwd_off[LH_BWD_DV])};
-    hipError_t e = launch_scatter_bwd(g, desc->dtype, dout, og, gidx, dog, dogT, Dv, st);
-    if (e == hipSuccess) {
-        AttnArgs a{g.BH, g.S, g.S_pad, g.d, softmax_scale(desc)};
-        e = launch_attn_bwd(a, desc->dtype, true, at(fwd_ws, P.fwd_off[LH_FWD_QG]), at(fwd_ws, P.fwd_off[LH_FWD_KG]),
-                            at(fwd_ws, P.fwd_off[LH_FWD_VG]), at(fwd_ws, P.fwd_off[LH_FWD_QT]),
-                            at(fwd_ws, P.fwd_off[LH_FWD_KT]), dog, dogT, lse, Dv, dxg[0], dxg[1], dxg[2], st);
-    }
+    hipError_t e = probed(LH_KERNEL_SCATTER_BWD, st, [&] {
+        return launch_scatter_bwd(g, desc->dtype, dout, og, gidx, dog, dogT, Dv, st);
+    });
+    const void* Qg = at(fwd_ws, P.fwd_off[LH_FWD_QG]);
+    const void* Kg = at(fwd_ws, P.fwd_off[LH_FWD_KG]);
+    const void* Vg = at(fwd_ws, P.fwd_off[LH_FWD_VG]);
+    AttnArgs a{g.BH, g.S, g.S_pad, g.d, softmax_scale(desc)};
+    if (e == hipSuccess)
+        e = probed(LH_KERNEL_ATTN_DKDV, st, [&] {
+            return launch_attn_dkdv(a, desc->dtype, true, Qg, Kg, Vg, at(fwd_ws, P.fwd_off[LH_FWD_QT]), dog, dogT,
+                                    lse, Dv, dxg[1], dxg[2], st);
+        });
+    if (e == hipSuccess)
+        e = probed(LH_KERNEL_ATTN_DQ, st, [&] {
+            return launch_attn_dq(a, desc->dtype, true, Qg, Kg, Vg, at(fwd_ws, P.fwd_off[LH_FWD_KT]), dog, lse, Dv,
+                                  dxg[0], st);
+        });
     if (e == hipSuccess) {
         const float* cg[3] = {dxg[0], dxg[1], dxg[2]};
         void* outs[3] = {dq, dk, dv};
-        e = launch_gather_pool_bwd(g, desc->dtype, cg, gpos, outs, st);
+        e = probed(LH_KERNEL_GATHER_POOL_BWD, st,
+                   [&] { return launch_gather_pool_bwd(g, desc->dtype, cg, gpos, outs, st); });
     }
     return dev(e);
 }
@@ -216,10 +246,12 @@ lh_status dense_causal_attn(const lh_desc* desc, const void* q, const void* k, c
     const int64_t BH = desc->B * desc->H, N = desc->N, N_pad = round64(N);
     const size_t dT = align_up((size_t)BH * desc->d * N_pad * esize(desc->dtype));
     float* o32 = (float*)at(ws, dT);
-    hipError_t e = launch_transpose(desc->dtype, BH, N, N_pad, desc->d, v, ws, st);
+    hipError_t e = probed(LH_KERNEL_TRANSPOSE, st,
+                          [&] { return launch_transpose(desc->dtype, BH, N, N_pad, desc->d, v, ws, st); });
     if (e == hipSuccess) {
         AttnArgs a{BH, N, N_pad, desc->d, softmax_scale(desc)};
-        e = launch_attn_fwd(a, desc->dtype, q, k, ws, o32, o, lse, st);
+        e = probed(LH_KERNEL_ATTN_FWD, st,
+                   [&] { return launch_attn_fwd(a, desc->dtype, q, k, ws, o32, o, lse, st); });
     }
     return dev(e);
 }
@@ -244,13 +276,28 @@ lh_status dense_causal_attn_backward(const lh_desc* desc, const void* q, const v
     const float* o32 = (const float*)at(fwd_ws, dT);
     hipError_t e = launch_transpose(desc->dtype, BH, N, N_pad, desc->d, q, qT, st);
     if (e == hipSuccess) e = launch_transpose(desc->dtype, BH, N, N_pad, desc->d, k, kT, st);
-    if (e == hipSuccess) e = launch_dense_bwd_prep(desc->dtype, BH, N, N_pad, desc->d, dout, o32, doT, Dv, st);
-    if (e == hipSuccess) {
-        AttnArgs a{BH, N, N_pad, desc->d, softmax_scale(desc)};
-        e = launch_attn_bwd(a, desc->dtype, desc->dtype == LH_F32, q, k, v, qT, kT, dout, doT, lse, Dv, dq, dk, dv,
-                            st);
-    }
+    if (e == hipSuccess)
+        e = probed(LH_KERNEL_DENSE_PREP, st, [&] {
+            return launch_dense_bwd_prep(desc->dtype, BH, N, N_pad, desc->d, dout, o32, doT, Dv, st);
+        });
+    AttnArgs a{BH, N, N_pad, desc->d, softmax_scale(desc)};
+    const bool f32 = desc->dtype == LH_F32;
+    if (e == hipSuccess)
+        e = probed(LH_KERNEL_ATTN_DKDV, st, [&] {
+            return launch_attn_dkdv(a, desc->dtype, f32, q, k, v, qT, dout, doT, lse, Dv, dk, dv, st);
+        });
+    if (e == hipSuccess)
+        e = probed(LH_KERNEL_ATTN_DQ, st,
+                   [&] { return launch_attn_dq(a, desc->dtype, f32, q, k, v, kT, dout, lse, Dv, dq, st); });
     return dev(e);
+}
+
+lh_status lh_set_probe(int kernel, void* start_event, void* stop_event) {
+    if (kernel < -1 || kernel >= LH_KERNEL_COUNT) return LH_E_ARG;
+    g_probe_kernel = (start_event && stop_event) ? kernel : -1;
+    g_probe_start = (hipEvent_t)start_event;
+    g_probe_stop = (hipEvent_t)stop_event;
+    return LH_OK;
 }
 
 }  // extern "C"

@@ -638,24 +638,28 @@ hipError_t fwd_t(const AttnArgs& a, const void* Q, const void* K, const void* VT
 }
 
 template <typename T, int D, typename OutT>
-hipError_t bwd_t(const AttnArgs& a, const void* Q, const void* K, const void* V, const void* QT, const void* KT,
-                 const void* dO, const void* dOT, const float* lse, const float* Dv, void* dQ, void* dK, void* dV,
-                 hipStream_t st) {
+hipError_t dkdv_t(const AttnArgs& a, const void* Q, const void* K, const void* V, const void* QT, const void* dO,
+                  const void* dOT, const float* lse, const float* Dv, void* dK, void* dV, hipStream_t st) {
     const AttnK k = make_k(a);
-    const size_t sh1 = dkdv_lds<T, D>();
-    static const hipError_t attr1 = hipFuncSetAttribute((const void*)attn_dkdv_kernel<T, D, OutT>,
-                                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)sh1);
-    (void)attr1;
-    attn_dkdv_kernel<T, D, OutT><<<dim3((unsigned)(k.nblk * a.BH)), kThreads, sh1, st>>>(
+    const size_t sh = dkdv_lds<T, D>();
+    static const hipError_t attr = hipFuncSetAttribute((const void*)attn_dkdv_kernel<T, D, OutT>,
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)sh);
+    (void)attr;
+    attn_dkdv_kernel<T, D, OutT><<<dim3((unsigned)(k.nblk * a.BH)), kThreads, sh, st>>>(
         (const T*)Q, (const T*)K, (const T*)V, (const T*)QT, (const T*)dO, (const T*)dOT, lse, Dv, (OutT*)dK,
         (OutT*)dV, k);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    const size_t sh2 = dq_lds<T, D>();
-    static const hipError_t attr2 = hipFuncSetAttribute((const void*)attn_dq_kernel<T, D, OutT>,
-                                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)sh2);
-    (void)attr2;
-    attn_dq_kernel<T, D, OutT><<<dim3((unsigned)(k.nblk * a.BH)), kThreads, sh2, st>>>(
+    return hipGetLastError();
+}
+
+template <typename T, int D, typename OutT>
+hipError_t dq_t(const AttnArgs& a, const void* Q, const void* K, const void* V, const void* KT, const void* dO,
+                const float* lse, const float* Dv, void* dQ, hipStream_t st) {
+    const AttnK k = make_k(a);
+    const size_t sh = dq_lds<T, D>();
+    static const hipError_t attr = hipFuncSetAttribute((const void*)attn_dq_kernel<T, D, OutT>,
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)sh);
+    (void)attr;
+    attn_dq_kernel<T, D, OutT><<<dim3((unsigned)(k.nblk * a.BH)), kThreads, sh, st>>>(
         (const T*)Q, (const T*)K, (const T*)V, (const T*)KT, (const T*)dO, lse, Dv, (OutT*)dQ, k);
     return hipGetLastError();
 }
@@ -669,14 +673,26 @@ hipError_t launch_attn_fwd(const AttnArgs& a, int dtype, const void* Q, const vo
     return fwd_t<float, 64>(a, Q, K, VT, O32, Ot, lse, st);   // f32 is built for d = 64 only
 }
 
-hipError_t launch_attn_bwd(const AttnArgs& a, int dtype, bool out_f32, const void* Q, const void* K, const void* V,
-                           const void* QT, const void* KT, const void* dO, const void* dOT, const float* lse,
-                           const float* Dv, void* dQ, void* dK, void* dV, hipStream_t st) {
-#define LH_BWD(T, D, O) bwd_t<T, D, O>(a, Q, K, V, QT, KT, dO, dOT, lse, Dv, dQ, dK, dV, st)
+hipError_t launch_attn_dkdv(const AttnArgs& a, int dtype, bool out_f32, const void* Q, const void* K, const void* V,
+                            const void* QT, const void* dO, const void* dOT, const float* lse, const float* Dv,
+                            void* dK, void* dV, hipStream_t st) {
+#define LH_DKDV(T, D, O) dkdv_t<T, D, O>(a, Q, K, V, QT, dO, dOT, lse, Dv, dK, dV, st)
     if (dtype == LH_BF16) {
-        if (a.d == 64) return out_f32 ? LH_BWD(bf16, 64, float) : LH_BWD(bf16, 64, bf16);
-        return out_f32 ? LH_BWD(bf16, 128, float) : LH_BWD(bf16, 128, bf16);
+        if (a.d == 64) return out_f32 ? LH_DKDV(bf16, 64, float) : LH_DKDV(bf16, 64, bf16);
+        return out_f32 ? LH_DKDV(bf16, 128, float) : LH_DKDV(bf16, 128, bf16);
     }
-    return LH_BWD(float, 64, float);   // f32 is built for d = 64 only
-#undef LH_BWD
+    return LH_DKDV(float, 64, float);   // f32 is built for d = 64 only
+#undef LH_DKDV
+}
+
+hipError_t launch_attn_dq(const AttnArgs& a, int dtype, bool out_f32, const void* Q, const void* K, const void* V,
+                          const void* KT, const void* dO, const float* lse, const float* Dv, void* dQ,
+                          hipStream_t st) {
+#define LH_DQ(T, D, O) dq_t<T, D, O>(a, Q, K, V, KT, dO, lse, Dv, dQ, st)
+    if (dtype == LH_BF16) {
+        if (a.d == 64) return out_f32 ? LH_DQ(bf16, 64, float) : LH_DQ(bf16, 64, bf16);
+        return out_f32 ? LH_DQ(bf16, 128, float) : LH_DQ(bf16, 128, bf16);
+    }
+    return LH_DQ(float, 64, float);
+#undef LH_DQ
 }

@@ -51,6 +51,9 @@ struct AttnArgs {
 hipError_t launch_attn_fwd(const AttnArgs& a, int dtype, const void* Q, const void* K, const void* VT, float* O32,
                            void* Ot, float* lse, hipStream_t st);
 // out_f32: dq/dk/dv are f32 (true) or the input dtype (false)
-hipError_t launch_attn_bwd(const AttnArgs& a, int dtype, bool out_f32, const void* Q, const void* K,
-                           const void* V, const void* QT, const void* KT, const void* dO, const void* dOT,
-                           const float* lse, const float* Dv, void* dQ, void* dK, void* dV, hipStream_t st);
+hipError_t launch_attn_dkdv(const AttnArgs& a, int dtype, bool out_f32, const void* Q, const void* K,
+                            const void* V, const void* QT, const void* dO, const void* dOT, const float* lse,
+                            const float* Dv, void* dK, void* dV, hipStream_t st);
+hipError_t launch_attn_dq(const AttnArgs& a, int dtype, bool out_f32, const void* Q, const void* K, const void* V,
+                          const void* KT, const void* dO, const float* lse, const float* Dv, void* dQ,
+                          hipStream_t st);

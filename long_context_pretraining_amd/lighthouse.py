@@ -61,7 +61,12 @@ _SIGS = {
     "dense_causal_attn_backward": [ctypes.POINTER(LhDesc), _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
                                    _SZ, _VP],
     "lh_status_string": [ctypes.c_int],
+    "lh_set_probe": [ctypes.c_int, _VP, _VP],
 }
+
+(KERNEL_POOL, KERNEL_SCORE, KERNEL_TOPK, KERNEL_MAP, KERNEL_GATHER, KERNEL_ATTN_FWD, KERNEL_SCATTER_FWD,
+ KERNEL_SCATTER_BWD, KERNEL_ATTN_DKDV, KERNEL_ATTN_DQ, KERNEL_GATHER_POOL_BWD, KERNEL_TRANSPOSE,
+ KERNEL_DENSE_PREP) = range(13)
 
 
 def header_functions() -> list:
@@ -85,6 +90,12 @@ def load_library():
         fn.restype = ctypes.c_char_p if name == "lh_status_string" else ctypes.c_int
     _lib = lib
     return lib
+
+
+def lh_set_probe(kernel: int, start_event, stop_event):
+    """Record raw hipEvent_t handles around every later launch of `kernel`
+    (-1 switches the hook off)."""
+    _check(load_library().lh_set_probe(kernel, start_event, stop_event), "lh_set_probe")
 
 
 def status_string(status: int) -> str:

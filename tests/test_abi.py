@@ -16,7 +16,7 @@ def test_exports_every_header_function():
     lib = lh.load_library()
     names = lh.header_functions()
     assert set(names) == {"lh_make_plan", "lh_pyramid", "lh_score_topk", "lh_forward", "lh_backward",
-                          "dense_causal_attn", "dense_causal_attn_backward", "lh_status_string"}
+                          "dense_causal_attn", "dense_causal_attn_backward", "lh_status_string", "lh_set_probe"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -105,3 +105,11 @@ def test_tensor_marshalling_rejects_host_tensors():
     t = torch.zeros(10)
     with pytest.raises(ValueError):
         lh.lh_pyramid(desc, t, t, t, t)
+
+
+def test_probe_hook_validates_kernel_id():
+    lib = lh.load_library()
+    assert lib.lh_set_probe(-1, None, None) == lh.LH_OK
+    assert lib.lh_set_probe(13, None, None) == lh.LH_E_ARG
+    assert lib.lh_set_probe(-2, None, None) == lh.LH_E_ARG
+    assert lib.lh_set_probe(lh.KERNEL_ATTN_DKDV, None, None) == lh.LH_OK   # null events: off
