@@ -124,7 +124,7 @@ __device__ __forceinline__ void split_frag(const floatx16& c, int cc, typename F
 // The output is written in f32 (and, when Ot is given, also in T).
 // ---------------------------------------------------------------------------
 template <typename T, int D>
-__global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K,
+__global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K,
                                                             const T* __restrict__ VT, float* __restrict__ O32,
                                                             T* __restrict__ Ot, float* __restrict__ LSE, AttnK a) {
     typedef typename Frag<T>::type F;
@@ -161,7 +161,13 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const T* __restrict_
     for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) o[cb][db] = floatx16{};
+    // Running reference max (log2 units) and row sum per query.  The output is
+    // rescaled only when the max grows by more than 2^8, so P stays below 256.
     float m_i[2] = {-INFINITY, -INFINITY}, l_i[2] = {0.f, 0.f};
+    const float c = a.scale_log2;
+    // last key each query may see, as an int32 offset from the tile
+    const int q_lim0 = (int)((q_base + col < S - 1 ? q_base + col : S - 1) - 4 * h);
+    const int q_lim1 = (int)((q_base + 32 + col < S - 1 ? q_base + 32 + col : S - 1) - 4 * h);
 
     KTile kt_r;
     VTile vt_r;
@@ -181,45 +187,46 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const T* __restrict_
         const T* lv = lk + KSZ;
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-            const int64_t kbase = (int64_t)t * kBN + 32 * ks;
+            const int kbase = t * kBN + 32 * ks;
             if (kbase > q_last_w) continue;
             floatx16 s[2] = {floatx16{}, floatx16{}};
 #pragma unroll
-            for (int c = 0; c < D / 16; ++c) {
-                const F kf = load8(lk + (32 * ks + col) * KTile::LD + 16 * c + 8 * h);
-                mma_k16(s[0], kf, qf[0][c]);
-                mma_k16(s[1], kf, qf[1][c]);
+            for (int cc = 0; cc < D / 16; ++cc) {
+                const F kf = load8(lk + (32 * ks + col) * KTile::LD + 16 * cc + 8 * h);
+                mma_k16(s[0], kf, qf[0][cc]);
+                mma_k16(s[1], kf, qf[1][cc]);
             }
-            const bool need_mask = (kbase + 31 > q_base) || (kbase + 31 >= S);
-#pragma unroll
-            for (int cb = 0; cb < 2; ++cb) {
-                const int64_t q = q_base + 32 * cb + col;
-                float mx = -INFINITY;
+            if (kbase + 31 > q_base || kbase + 31 >= S) {   // diagonal or tail: mask key > query / key >= S
+                const int l0 = q_lim0 - kbase, l1 = q_lim1 - kbase;
 #pragma unroll
                 for (int j = 0; j < 16; ++j) {
-                    float v = s[cb][j] * a.scale_log2;
-                    if (need_mask) {
-                        const int64_t key = kbase + c_row(j, h);
-                        if (key > q || key >= S) v = -INFINITY;
-                    }
-                    s[cb][j] = v;
-                    mx = fmaxf(mx, v);
+                    if (c_row0(j) > l0) s[0][j] = -INFINITY;
+                    if (c_row0(j) > l1) s[1][j] = -INFINITY;
                 }
-                mx = fmaxf(mx, xor32(mx));
-                const float m_new = fmaxf(m_i[cb], mx);
-                const float m_use = m_new == -INFINITY ? 0.f : m_new;
-                const float alpha = fast_exp2(m_i[cb] - m_use);
+            }
+#pragma unroll
+            for (int cb = 0; cb < 2; ++cb) {
+                float mx = fmaxf(s[cb][0], s[cb][1]);
+#pragma unroll
+                for (int j = 2; j < 16; j += 2) mx = fmaxf(mx, fmaxf(s[cb][j], s[cb][j + 1]));
+                mx = max_halves(mx) * c;
+                if (wave_any(mx > m_i[cb] + 8.f)) {
+                    const float m_new = fmaxf(m_i[cb], mx);
+                    const float alpha = m_new == m_i[cb] ? 1.f : fast_exp2(m_i[cb] - m_new);
+                    m_i[cb] = m_new;
+                    l_i[cb] *= alpha;
+#pragma unroll
+                    for (int db = 0; db < D / 32; ++db) o[cb][db] *= alpha;
+                }
+                const float neg = m_i[cb] == -INFINITY ? 0.f : -m_i[cb];
                 float rs = 0.f;
 #pragma unroll
                 for (int j = 0; j < 16; ++j) {
-                    const float p = fast_exp2(s[cb][j] - m_use);
-                    s[cb][j] = p;
-                    rs += p;
+                    const float pv = fast_exp2(fmaf(s[cb][j], c, neg));
+                    s[cb][j] = pv;
+                    rs += pv;
                 }
-                l_i[cb] = l_i[cb] * alpha + rs;
-                m_i[cb] = m_new;
-#pragma unroll
-                for (int db = 0; db < D / 32; ++db) o[cb][db] *= alpha;
+                l_i[cb] += rs;
             }
 #pragma unroll
             for (int c2 = 0; c2 < 2; ++c2) {
@@ -249,7 +256,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const T* __restrict_
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb) {
         const int64_t q = q_base + 32 * cb + col;
-        const float l = l_i[cb] + xor32(l_i[cb]);
+        const float l = sum_halves(l_i[cb]);
         const float inv = 1.f / l;
         if (q < S) {
             float* orow = O32 + (bh * S + q) * D;
@@ -329,6 +336,8 @@ __global__ __launch_bounds__(kThreads) void attn_dq_kernel(const T* __restrict__
     for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) acc[cb][db] = floatx16{};
+    const int q_lim0 = (int)((q_base + col < S - 1 ? q_base + col : S - 1) - 4 * h);
+    const int q_lim1 = (int)((q_base + 32 + col < S - 1 ? q_base + 32 + col : S - 1) - 4 * h);
 
     RT kr, vr;
     CT ktr;
@@ -364,21 +373,21 @@ __global__ __launch_bounds__(kThreads) void attn_dq_kernel(const T* __restrict__
                 mma_k16(dp[0], vf, df[0][c]);
                 mma_k16(dp[1], vf, df[1][c]);
             }
-            const bool need_mask = (kbase + 31 > q_base) || (kbase + 31 >= S);
-#pragma unroll
-            for (int cb = 0; cb < 2; ++cb) {
-                const int64_t q = q_base + 32 * cb + col;
-                const bool qok = q < S;
+            if (kbase + 31 > q_base || kbase + 31 >= S) {   // diagonal or tail
+                const int l0 = q_lim0 - (int)kbase, l1 = q_lim1 - (int)kbase;
 #pragma unroll
                 for (int j = 0; j < 16; ++j) {
-                    float p = fast_exp2(s[cb][j] * a.scale_log2 - lse2[cb]);
-                    if (need_mask) {
-                        const int64_t key = kbase + c_row(j, h);
-                        if (key > q || key >= S || !qok) p = 0.f;
-                    }
-                    s[cb][j] = p * (dp[cb][j] - dd[cb]);
+                    if (c_row0(j) > l0) s[0][j] = -INFINITY;
+                    if (c_row0(j) > l1) s[1][j] = -INFINITY;
                 }
             }
+#pragma unroll
+            for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+                for (int j = 0; j < 16; ++j) {
+                    const float pv = fast_exp2(fmaf(s[cb][j], a.scale_log2, -lse2[cb]));
+                    s[cb][j] = pv * (dp[cb][j] - dd[cb]);
+                }
 #pragma unroll
             for (int c2 = 0; c2 < 2; ++c2) {
                 F g0, g1, r0, r1;
@@ -549,15 +558,17 @@ __global__ __launch_bounds__(kThreads) void attn_dkdv_kernel(const T* __restrict
                     mma_k16(s, qa[c], kf[kc][c]);
                     mma_k16(dp, da[c], vf[kc][c]);
                 }
-                const int64_t key = k_base + 32 * kc + col;
-                const bool need_mask = (k_base + 32 * kc + 31 > q0) || (q0 + 31 >= S);
+                if (k_base + 32 * kc + 31 > q0 || q0 + 31 >= S) {   // diagonal or tail
+                    // row j (query q0 + 4h + c_row0(j)) is masked when the key is after it or it is past S
+                    const int kl = (int)(k_base + 32 * kc + col - q0) - 4 * h;
+                    const int sl = (int)(S - q0) - 4 * h;
+#pragma unroll
+                    for (int j = 0; j < 16; ++j)
+                        if (c_row0(j) < kl || c_row0(j) >= sl) s[j] = -INFINITY;
+                }
 #pragma unroll
                 for (int j = 0; j < 16; ++j) {
-                    float pv = fast_exp2(s[j] * a.scale_log2 - lrow[j]);
-                    if (need_mask) {
-                        const int64_t q = q0 + c_row(j, h);
-                        if (key > q || q >= S) pv = 0.f;
-                    }
+                    const float pv = fast_exp2(fmaf(s[j], a.scale_log2, -lrow[j]));
                     p[kc][j] = pv;
                     ds[kc][j] = pv * (dp[j] - drow[j]);
                 }

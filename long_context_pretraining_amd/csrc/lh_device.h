@@ -74,8 +74,21 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 
 template <typename T> __device__ __forceinline__ float to_f(T x) { return static_cast<float>(x); }
 
-// Wave-wide helpers (wave64).
-__device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
+// Wave-wide helpers (wave64).  v_permlane32_swap exchanges the two 32-lane
+// halves, so combining its two results gives the reduction over lanes l and
+// l ^ 32 in every lane with one cross-lane instruction.
+__device__ __forceinline__ float max_halves(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_halves(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
+
+// Row offset (within a 32-row C tile) of register j, without the 4*(l/32) term.
+__device__ __forceinline__ constexpr int c_row0(int j) { return 8 * (j >> 2) + (j & 3); }
 
 // Sixteen bytes of T.
 template <typename T> struct V16;
