@@ -101,23 +101,12 @@ __device__ __forceinline__ void block_order(const AttnK& a, bool longest_last_ro
 }
 
 // The bf16 forward multiplies V by P in two parts, P = hi + lo with hi the
-// bf16 rounding of P and lo the bf16 rounding of the remainder, so that the
-// f32 output carries P to about 2^-17 relative.  Without it the output would
-// use P rounded to 8 bits while the backward recomputes P in f32, and
-// D = rowsum(dO * O) would then be off by ~2^-9 |dP| in rows dominated by a
-// few keys -- an error the products with K and Q magnify.
+// bf16 rounding of P and lo the bf16 rounding of the remainder (split_frag),
+// so that the f32 output carries P to about 2^-17 relative.  Without it the
+// output would use P rounded to 8 bits while the backward recomputes P in
+// f32, and D = rowsum(dO * O) would then be off by ~2^-9 |dP| in rows
+// dominated by a few keys -- an error the products with K and Q magnify.
 template <typename T> constexpr bool kSplitP = sizeof(T) == 2;
-
-template <typename T>
-__device__ __forceinline__ void split_frag(const floatx16& c, int cc, typename Frag<T>::type& hi,
-                                          typename Frag<T>::type& lo) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const float x = c[8 * cc + e];
-        hi[e] = static_cast<T>(x);
-        if (kSplitP<T>) lo[e] = static_cast<T>(x - static_cast<float>(hi[e]));
-    }
-}
 
 // ---------------------------------------------------------------------------
 // Forward: O = softmax(scale Q K^T, causal) V and LSE, per 256-query block.
@@ -206,10 +195,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const T* __restri
             }
 #pragma unroll
             for (int cb = 0; cb < 2; ++cb) {
-                float mx = fmaxf(s[cb][0], s[cb][1]);
-#pragma unroll
-                for (int j = 2; j < 16; j += 2) mx = fmaxf(mx, fmaxf(s[cb][j], s[cb][j + 1]));
-                mx = max_halves(mx) * c;
+                const float mx = max_halves(max16(s[cb])) * c;
                 if (wave_any(mx > m_i[cb] + 8.f)) {
                     const float m_new = fmaxf(m_i[cb], mx);
                     const float alpha = m_new == m_i[cb] ? 1.f : fast_exp2(m_i[cb] - m_new);
@@ -288,7 +274,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const T* __restri
 // noise.  bf16 therefore feeds dS as hi + lo parts (as P in the forward).
 // ---------------------------------------------------------------------------
 template <typename T, int D, typename OutT>
-__global__ __launch_bounds__(kThreads) void attn_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K,
+__global__ __launch_bounds__(kThreads, 2) void attn_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K,
                                                            const T* __restrict__ V, const T* __restrict__ KT,
                                                            const T* __restrict__ dO, const float* __restrict__ LSE,
                                                            const float* __restrict__ Dv, OutT* __restrict__ dQ,
@@ -534,9 +520,9 @@ __global__ __launch_bounds__(kThreads) void attn_dkdv_kernel(const T* __restrict
             if (k_base > q0 + 31 || k_base >= S) continue;   // every key of this wave after every query
             F qa[D / 16], da[D / 16];
 #pragma unroll
-            for (int c = 0; c < D / 16; ++c) {
-                qa[c] = load8(lq + (32 * qs + col) * RT::LD + 16 * c + 8 * h);
-                da[c] = load8(ldo + (32 * qs + col) * RT::LD + 16 * c + 8 * h);
+            for (int cc = 0; cc < D / 16; ++cc) {
+                qa[cc] = load8(lq + (32 * qs + col) * RT::LD + 16 * cc + 8 * h);
+                da[cc] = load8(ldo + (32 * qs + col) * RT::LD + 16 * cc + 8 * h);
             }
             float lrow[16], drow[16];
 #pragma unroll
@@ -549,14 +535,13 @@ __global__ __launch_bounds__(kThreads) void attn_dkdv_kernel(const T* __restrict
                     drow[4 * m + i] = d4[i];
                 }
             }
-            floatx16 p[2], ds[2];
 #pragma unroll
             for (int kc = 0; kc < 2; ++kc) {
-                floatx16 s = floatx16{}, dp = floatx16{};
+                floatx16 sp = floatx16{}, dp = floatx16{};
 #pragma unroll
-                for (int c = 0; c < D / 16; ++c) {
-                    mma_k16(s, qa[c], kf[kc][c]);
-                    mma_k16(dp, da[c], vf[kc][c]);
+                for (int cc = 0; cc < D / 16; ++cc) {
+                    mma_k16(sp, qa[cc], kf[kc][cc]);
+                    mma_k16(dp, da[cc], vf[kc][cc]);
                 }
                 if (k_base + 32 * kc + 31 > q0 || q0 + 31 >= S) {   // diagonal or tail
                     // row j (query q0 + 4h + c_row0(j)) is masked when the key is after it or it is past S
@@ -564,35 +549,29 @@ __global__ __launch_bounds__(kThreads) void attn_dkdv_kernel(const T* __restrict
                     const int sl = (int)(S - q0) - 4 * h;
 #pragma unroll
                     for (int j = 0; j < 16; ++j)
-                        if (c_row0(j) < kl || c_row0(j) >= sl) s[j] = -INFINITY;
+                        if (c_row0(j) < kl || c_row0(j) >= sl) sp[j] = -INFINITY;
                 }
 #pragma unroll
                 for (int j = 0; j < 16; ++j) {
-                    const float pv = fast_exp2(fmaf(s[j], a.scale_log2, -lrow[j]));
-                    p[kc][j] = pv;
-                    ds[kc][j] = pv * (dp[j] - drow[j]);
+                    const float pv = fast_exp2(fmaf(sp[j], a.scale_log2, -lrow[j]));
+                    sp[j] = pv;
+                    dp[j] = pv * (dp[j] - drow[j]);
                 }
-            }
 #pragma unroll
-            for (int c2 = 0; c2 < 2; ++c2) {
-                F p0, p1, g0, g1, p0r, p1r, g0r, g1r;
-                split_frag<T>(p[0], c2, p0, p0r);
-                split_frag<T>(p[1], c2, p1, p1r);
-                split_frag<T>(ds[0], c2, g0, g0r);
-                split_frag<T>(ds[1], c2, g1, g1r);
+                for (int c2 = 0; c2 < 2; ++c2) {
+                    F ph, pl, gh, gl;
+                    split_frag<T>(sp, c2, ph, pl);
+                    split_frag<T>(dp, c2, gh, gl);
 #pragma unroll
-                for (int db = 0; db < D / 32; ++db) {
-                    const F dof = load_4_4(ldot + (32 * db + col) * CT::LD + 32 * qs + 16 * c2 + 4 * h);
-                    const F qtf = load_4_4(lqt + (32 * db + col) * CT::LD + 32 * qs + 16 * c2 + 4 * h);
-                    mma_k16(dv[0][db], dof, p0);
-                    mma_k16(dv[1][db], dof, p1);
-                    mma_k16(dk[0][db], qtf, g0);
-                    mma_k16(dk[1][db], qtf, g1);
-                    if (kSplitP<T>) {
-                        mma_k16(dv[0][db], dof, p0r);
-                        mma_k16(dv[1][db], dof, p1r);
-                        mma_k16(dk[0][db], qtf, g0r);
-                        mma_k16(dk[1][db], qtf, g1r);
+                    for (int db = 0; db < D / 32; ++db) {
+                        const F dof = load_4_4(ldot + (32 * db + col) * CT::LD + 32 * qs + 16 * c2 + 4 * h);
+                        const F qtf = load_4_4(lqt + (32 * db + col) * CT::LD + 32 * qs + 16 * c2 + 4 * h);
+                        mma_k16(dv[kc][db], dof, ph);
+                        mma_k16(dk[kc][db], qtf, gh);
+                        if (kSplitP<T>) {
+                            mma_k16(dv[kc][db], dof, pl);
+                            mma_k16(dk[kc][db], qtf, gl);
+                        }
                     }
                 }
             }

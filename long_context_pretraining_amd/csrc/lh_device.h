@@ -58,13 +58,71 @@ __device__ __forceinline__ typename Frag<T>::type load_4_4(const T* p) {
     return r;
 }
 
-// Registers 8c .. 8c+7 of a C tile as a B-operand fragment of type T.
+typedef float floatx2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Registers 8c .. 8c+7 of a C tile as a B-operand fragment of type T
+// (bf16: four paired round-to-nearest-even conversions).
 template <typename T>
-__device__ __forceinline__ typename Frag<T>::type c_to_frag(const floatx16& c, int cc) {
-    typename Frag<T>::type r;
+__device__ __forceinline__ typename Frag<T>::type c_to_frag(const floatx16& c, int cc);
+template <>
+__device__ __forceinline__ bf16x8 c_to_frag<bf16>(const floatx16& c, int cc) {
+    bf16x8 r;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) r[e] = static_cast<T>(c[8 * cc + e]);
+    for (int e = 0; e < 4; ++e) {
+        const bf16x2 h = __builtin_convertvector((floatx2){c[8 * cc + 2 * e], c[8 * cc + 2 * e + 1]}, bf16x2);
+        r[2 * e] = h[0];
+        r[2 * e + 1] = h[1];
+    }
     return r;
+}
+template <>
+__device__ __forceinline__ floatx8 c_to_frag<float>(const floatx16& c, int cc) {
+    floatx8 r;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) r[e] = c[8 * cc + e];
+    return r;
+}
+
+// Registers 8c .. 8c+7 as hi + lo bf16 fragments: hi = RNE(x), lo = RNE(x - hi).
+// x - hi is exact in f32 and comes from one dot2 against (-1, 0) or (0, -1),
+// so the split costs two VALU operations per element.  For f32 the fragment
+// is exact and lo is unused.
+template <typename T>
+__device__ __forceinline__ void split_frag(const floatx16& c, int cc, typename Frag<T>::type& hi,
+                                          typename Frag<T>::type& lo);
+template <>
+__device__ __forceinline__ void split_frag<bf16>(const floatx16& c, int cc, bf16x8& hi, bf16x8& lo) {
+    // (-1, -0) rather than (-1, 0): the compiler turns the pair (-1, 0) into the
+    // inline constant -1.0, which the hardware reads as the f32 bit pattern,
+    // i.e. the pair (0, -1).  -0 keeps it a literal and adds nothing.
+    const bf16x2 sel0 = {(bf16)-1.0f, (bf16)-0.0f}, sel1 = {(bf16)0.0f, (bf16)-1.0f};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const float x0 = c[8 * cc + 2 * e], x1 = c[8 * cc + 2 * e + 1];
+        const bf16x2 h = __builtin_convertvector((floatx2){x0, x1}, bf16x2);
+        const float r0 = __builtin_amdgcn_fdot2_f32_bf16(h, sel0, x0, false);
+        const float r1 = __builtin_amdgcn_fdot2_f32_bf16(h, sel1, x1, false);
+        const bf16x2 l = __builtin_convertvector((floatx2){r0, r1}, bf16x2);
+        hi[2 * e] = h[0];
+        hi[2 * e + 1] = h[1];
+        lo[2 * e] = l[0];
+        lo[2 * e + 1] = l[1];
+    }
+}
+template <>
+__device__ __forceinline__ void split_frag<float>(const floatx16& c, int cc, floatx8& hi, floatx8& lo) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) hi[e] = c[8 * cc + e];
+    lo = hi;
+}
+
+// max over the 16 registers of a C tile (eight 3-input maxima)
+__device__ __forceinline__ float max16(const floatx16& v) {
+    float m = __builtin_fmaxf(v[0], v[1]);
+#pragma unroll
+    for (int j = 2; j < 16; j += 2) m = __builtin_fmaxf(__builtin_fmaxf(m, v[j]), v[j + 1]);
+    return m;
 }
 
 // Row (within a 32-row C tile) held by register j of lane-half h.
