@@ -37,61 +37,63 @@ struct AttnK {
     int nblk;   // row blocks per head
 };
 
-template <typename T> struct Pad { enum { ROW = 16 / (int)sizeof(T), COLT = 4 }; };
+// ---------------------------------------------------------------------------
+// LDS tiles.  A tile is ROWS rows of ROWB bytes, filled straight from global
+// memory by global_load_lds (16 bytes per lane, 1 KB per wave instruction, no
+// staging registers).  16-byte chunk c of row r sits at chunk c ^ (r & 7) of
+// that row, so the 8 lanes of one LDS phase that read the same chunk of 8
+// consecutive rows hit 8 different bank groups.
+// Row tiles hold 64 rows of a row-major [S][D] array (rows past S repeat row
+// S-1; the masks make them irrelevant).  Column tiles hold D rows of a
+// transposed [D][S_pad] array, 64 keys each, in the slot order the gather and
+// transposes write (see store_transposed): lane half h then finds the 8 keys
+// of its k16 step as one 16-byte run.
+// ---------------------------------------------------------------------------
+typedef __attribute__((address_space(3))) void lds_void;
 
-// Cooperative copy of a [64 x D] row-major tile (rows r0.., bounds-checked
-// against S) into LDS (stride D + pad) through registers.
-template <typename T, int D>
-struct RowTile {
-    typedef typename Frag<T>::type F;
-    static constexpr int LD = D + Pad<T>::ROW;
-    static constexpr int UNITS = kBN * D / 8 / kThreads;   // 8-element units per thread
-    F r[UNITS];
-    __device__ __forceinline__ void load(const T* base, int64_t r0, int64_t S) {
-#pragma unroll
-        for (int u = 0; u < UNITS; ++u) {
-            const int id = threadIdx.x + u * kThreads;
-            const int row = id / (D / 8), col = (id % (D / 8)) * 8;
-            r[u] = load8_or_zero(base + (r0 + row) * D + col, r0 + row < S);
-        }
-    }
-    __device__ __forceinline__ void store(T* lds) const {
-#pragma unroll
-        for (int u = 0; u < UNITS; ++u) {
-            const int id = threadIdx.x + u * kThreads;
-            const int row = id / (D / 8), col = (id % (D / 8)) * 8;
-            *reinterpret_cast<F*>(lds + row * LD + col) = r[u];
-        }
-    }
-};
+template <int ROWB>
+__device__ __forceinline__ int swz(int row, int chunk) { return row * ROWB + ((chunk ^ (row & 7)) << 4); }
 
-// Cooperative copy of a [D x 64] slice (columns c0.. of a transposed array
-// with row length S_pad; always in bounds) into LDS (stride 64 + 4).
-template <typename T, int D>
-struct ColTile {
-    typedef typename Frag<T>::type F;
-    typedef typename Frag<T>::half Hf;
-    static constexpr int LD = kBN + Pad<T>::COLT;
-    static constexpr int UNITS = kBN * D / 8 / kThreads;
-    F r[UNITS];
-    __device__ __forceinline__ void load(const T* base, int64_t c0, int64_t S_pad) {
+template <int ROWB, int BYTES, class RowPtr>
+__device__ __forceinline__ void stage_tile(unsigned char* tile, RowPtr row_ptr) {
+    static_assert(BYTES % 4096 == 0, "tile must split into 1 KB wave instructions");
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
-        for (int u = 0; u < UNITS; ++u) {
-            const int id = threadIdx.x + u * kThreads;
-            const int row = id / (kBN / 8), col = (id % (kBN / 8)) * 8;
-            r[u] = load8(base + row * S_pad + c0 + col);
-        }
+    for (int i = 0; i < BYTES / 4096; ++i) {
+        const int base = (wave * (BYTES / 4096) + i) * 1024;
+        const int pos = base + 16 * lane;
+        const int row = pos / ROWB;
+        const int chunk = ((pos % ROWB) >> 4) ^ (row & 7);
+        const unsigned char* g = reinterpret_cast<const unsigned char*>(row_ptr(row)) + (chunk << 4);
+        __builtin_amdgcn_global_load_lds(g, (lds_void*)(tile + base), 16, 0, 0);
     }
-    __device__ __forceinline__ void store(T* lds) const {
-#pragma unroll
-        for (int u = 0; u < UNITS; ++u) {
-            const int id = threadIdx.x + u * kThreads;
-            const int row = id / (kBN / 8), col = (id % (kBN / 8)) * 8;
-            *reinterpret_cast<Hf*>(lds + row * LD + col) = r[u].lo;
-            *reinterpret_cast<Hf*>(lds + row * LD + col + 4) = r[u].hi;
-        }
-    }
-};
+}
+
+// 8 elements of T starting at element e0 (a multiple of 8) of a tile row.
+template <typename T, int ROWB>
+__device__ __forceinline__ typename Frag<T>::type tile_frag(const unsigned char* tile, int row, int e0);
+template <>
+__device__ __forceinline__ bf16x8 tile_frag<bf16, 128>(const unsigned char* tile, int row, int e0) {
+    return *reinterpret_cast<const bf16x8*>(tile + swz<128>(row, e0 >> 3));
+}
+template <>
+__device__ __forceinline__ bf16x8 tile_frag<bf16, 256>(const unsigned char* tile, int row, int e0) {
+    return *reinterpret_cast<const bf16x8*>(tile + swz<256>(row, e0 >> 3));
+}
+template <>
+__device__ __forceinline__ floatx8 tile_frag<float, 256>(const unsigned char* tile, int row, int e0) {
+    const floatx4 a = *reinterpret_cast<const floatx4*>(tile + swz<256>(row, e0 >> 2));
+    const floatx4 b = *reinterpret_cast<const floatx4*>(tile + swz<256>(row, (e0 >> 2) + 1));
+    floatx8 r;
+    r.lo = a;
+    r.hi = b;
+    return r;
+}
+
+__device__ __forceinline__ void wait_tiles_and_sync() {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+}
 
 __device__ __forceinline__ void block_order(const AttnK& a, bool longest_last_rows, int64_t& bh, int& blk) {
     const int64_t x = blockIdx.x;
@@ -117,11 +119,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const T* __restri
                                                             const T* __restrict__ VT, float* __restrict__ O32,
                                                             T* __restrict__ Ot, float* __restrict__ LSE, AttnK a) {
     typedef typename Frag<T>::type F;
-    typedef RowTile<T, D> KTile;
-    typedef ColTile<T, D> VTile;
-    constexpr int KSZ = kBN * KTile::LD, VSZ = D * VTile::LD;
+    constexpr int KROWB = D * (int)sizeof(T), VROWB = kBN * (int)sizeof(T);
+    constexpr int KBYTES = kBN * KROWB, VBYTES = D * VROWB, BUF = KBYTES + VBYTES;
     extern __shared__ __align__(16) unsigned char smem[];
-    T* lds = reinterpret_cast<T*>(smem);
 
     int64_t bh; int qb;
     block_order(a, true, bh, qb);
@@ -158,22 +158,21 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const T* __restri
     const int q_lim0 = (int)((q_base + col < S - 1 ? q_base + col : S - 1) - 4 * h);
     const int q_lim1 = (int)((q_base + 32 + col < S - 1 ? q_base + 32 + col : S - 1) - 4 * h);
 
-    KTile kt_r;
-    VTile vt_r;
-    kt_r.load(Kh, 0, S);
-    vt_r.load(VTh, 0, a.S_pad);
-    kt_r.store(lds);
-    vt_r.store(lds + KSZ);
-    __syncthreads();
+    auto stage = [&](int t, unsigned char* b) {
+        stage_tile<KROWB, KBYTES>(b, [&](int r) {
+            const int64_t row = (int64_t)t * kBN + r;
+            return Kh + (row < S ? row : S - 1) * D;
+        });
+        stage_tile<VROWB, VBYTES>(b + KBYTES, [&](int r) { return VTh + r * a.S_pad + (int64_t)t * kBN; });
+    };
+    stage(0, smem);
+    wait_tiles_and_sync();
 
     for (int t = 0; t < ntiles; ++t) {
         const int buf = t & 1;
-        if (t + 1 < ntiles) {
-            kt_r.load(Kh, (int64_t)(t + 1) * kBN, S);
-            vt_r.load(VTh, (int64_t)(t + 1) * kBN, a.S_pad);
-        }
-        const T* lk = lds + buf * (KSZ + VSZ);
-        const T* lv = lk + KSZ;
+        if (t + 1 < ntiles) stage(t + 1, smem + (buf ^ 1) * BUF);
+        const unsigned char* lk = smem + buf * BUF;
+        const unsigned char* lv = lk + KBYTES;
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
             const int kbase = t * kBN + 32 * ks;
@@ -181,7 +180,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const T* __restri
             floatx16 s[2] = {floatx16{}, floatx16{}};
 #pragma unroll
             for (int cc = 0; cc < D / 16; ++cc) {
-                const F kf = load8(lk + (32 * ks + col) * KTile::LD + 16 * cc + 8 * h);
+                const F kf = tile_frag<T, KROWB>(lk, 32 * ks + col, 16 * cc + 8 * h);
                 mma_k16(s[0], kf, qf[0][cc]);
                 mma_k16(s[1], kf, qf[1][cc]);
             }
@@ -221,7 +220,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const T* __restri
                 split_frag<T>(s[1], c2, p1, r1);
 #pragma unroll
                 for (int db = 0; db < D / 32; ++db) {
-                    const F vf = load_4_4(lv + (32 * db + col) * VTile::LD + 32 * ks + 16 * c2 + 4 * h);
+                    const F vf = tile_frag<T, VROWB>(lv, 32 * db + col, 32 * ks + 16 * c2 + 8 * h);
                     mma_k16(o[0][db], vf, p0);
                     mma_k16(o[1][db], vf, p1);
                     if (kSplitP<T>) {
@@ -231,12 +230,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const T* __restri
                 }
             }
         }
-        if (t + 1 < ntiles) {
-            T* nb = lds + (buf ^ 1) * (KSZ + VSZ);
-            kt_r.store(nb);
-            vt_r.store(nb + KSZ);
-        }
-        __syncthreads();
+        wait_tiles_and_sync();
     }
 
 #pragma unroll
@@ -280,11 +274,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_dq_kernel(const T* __restric
                                                            const float* __restrict__ Dv, OutT* __restrict__ dQ,
                                                            AttnK a) {
     typedef typename Frag<T>::type F;
-    typedef RowTile<T, D> RT;
-    typedef ColTile<T, D> CT;
-    constexpr int RSZ = kBN * RT::LD, CSZ = D * CT::LD, BUF = 2 * RSZ + CSZ;
+    constexpr int RROWB = D * (int)sizeof(T), CROWB = kBN * (int)sizeof(T);
+    constexpr int RBYTES = kBN * RROWB, CBYTES = D * CROWB, BUF = 2 * RBYTES + CBYTES;
     extern __shared__ __align__(16) unsigned char smem[];
-    T* lds = reinterpret_cast<T*>(smem);
 
     int64_t bh; int qb;
     block_order(a, true, bh, qb);
@@ -325,26 +317,24 @@ __global__ __launch_bounds__(kThreads, 2) void attn_dq_kernel(const T* __restric
     const int q_lim0 = (int)((q_base + col < S - 1 ? q_base + col : S - 1) - 4 * h);
     const int q_lim1 = (int)((q_base + 32 + col < S - 1 ? q_base + 32 + col : S - 1) - 4 * h);
 
-    RT kr, vr;
-    CT ktr;
-    kr.load(Kh, 0, S);
-    vr.load(Vh, 0, S);
-    ktr.load(KTh, 0, a.S_pad);
-    kr.store(lds);
-    vr.store(lds + RSZ);
-    ktr.store(lds + 2 * RSZ);
-    __syncthreads();
+    auto stage = [&](int t, unsigned char* b) {
+        auto clamp = [&](int r) {
+            const int64_t row = (int64_t)t * kBN + r;
+            return row < S ? row : S - 1;
+        };
+        stage_tile<RROWB, RBYTES>(b, [&](int r) { return Kh + clamp(r) * D; });
+        stage_tile<RROWB, RBYTES>(b + RBYTES, [&](int r) { return Vh + clamp(r) * D; });
+        stage_tile<CROWB, CBYTES>(b + 2 * RBYTES, [&](int r) { return KTh + r * a.S_pad + (int64_t)t * kBN; });
+    };
+    stage(0, smem);
+    wait_tiles_and_sync();
 
     for (int t = 0; t < ntiles; ++t) {
         const int buf = t & 1;
-        if (t + 1 < ntiles) {
-            kr.load(Kh, (int64_t)(t + 1) * kBN, S);
-            vr.load(Vh, (int64_t)(t + 1) * kBN, S);
-            ktr.load(KTh, (int64_t)(t + 1) * kBN, a.S_pad);
-        }
-        const T* lk = lds + buf * BUF;
-        const T* lv = lk + RSZ;
-        const T* lkt = lk + 2 * RSZ;
+        if (t + 1 < ntiles) stage(t + 1, smem + (buf ^ 1) * BUF);
+        const unsigned char* lk = smem + buf * BUF;
+        const unsigned char* lv = lk + RBYTES;
+        const unsigned char* lkt = lk + 2 * RBYTES;
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
             const int64_t kbase = (int64_t)t * kBN + 32 * ks;
@@ -352,8 +342,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_dq_kernel(const T* __restric
             floatx16 s[2] = {floatx16{}, floatx16{}}, dp[2] = {floatx16{}, floatx16{}};
 #pragma unroll
             for (int c = 0; c < D / 16; ++c) {
-                const F kf = load8(lk + (32 * ks + col) * RT::LD + 16 * c + 8 * h);
-                const F vf = load8(lv + (32 * ks + col) * RT::LD + 16 * c + 8 * h);
+                const F kf = tile_frag<T, RROWB>(lk, 32 * ks + col, 16 * c + 8 * h);
+                const F vf = tile_frag<T, RROWB>(lv, 32 * ks + col, 16 * c + 8 * h);
                 mma_k16(s[0], kf, qf[0][c]);
                 mma_k16(s[1], kf, qf[1][c]);
                 mma_k16(dp[0], vf, df[0][c]);
@@ -381,7 +371,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_dq_kernel(const T* __restric
                 split_frag<T>(s[1], c2, g1, r1);
 #pragma unroll
                 for (int db = 0; db < D / 32; ++db) {
-                    const F kf = load_4_4(lkt + (32 * db + col) * CT::LD + 32 * ks + 16 * c2 + 4 * h);
+                    const F kf = tile_frag<T, CROWB>(lkt, 32 * db + col, 32 * ks + 16 * c2 + 8 * h);
                     mma_k16(acc[0][db], kf, g0);
                     mma_k16(acc[1][db], kf, g1);
                     if (kSplitP<T>) {
@@ -391,13 +381,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_dq_kernel(const T* __restric
                 }
             }
         }
-        if (t + 1 < ntiles) {
-            T* nb = lds + (buf ^ 1) * BUF;
-            kr.store(nb);
-            vr.store(nb + RSZ);
-            ktr.store(nb + 2 * RSZ);
-        }
-        __syncthreads();
+        wait_tiles_and_sync();
     }
 
 #pragma unroll
@@ -428,12 +412,10 @@ __global__ __launch_bounds__(kThreads) void attn_dkdv_kernel(const T* __restrict
                                                              const float* __restrict__ Dv, OutT* __restrict__ dK,
                                                              OutT* __restrict__ dV, AttnK a) {
     typedef typename Frag<T>::type F;
-    typedef RowTile<T, D> RT;
-    typedef ColTile<T, D> CT;
-    constexpr int RSZ = kBN * RT::LD, CSZ = D * CT::LD;
-    constexpr int BUF = 2 * RSZ + 2 * CSZ + 2 * kBN * (int)(sizeof(float) / sizeof(T));
+    constexpr int RROWB = D * (int)sizeof(T), CROWB = kBN * (int)sizeof(T);
+    constexpr int RBYTES = kBN * RROWB, CBYTES = D * CROWB;
+    constexpr int OFF_F = 2 * RBYTES + 2 * CBYTES, BUF = OFF_F + 2 * kBN * 4;
     extern __shared__ __align__(16) unsigned char smem[];
-    T* lds = reinterpret_cast<T*>(smem);
 
     int64_t bh; int kb;
     block_order(a, false, bh, kb);
@@ -473,47 +455,35 @@ __global__ __launch_bounds__(kThreads) void attn_dkdv_kernel(const T* __restrict
             dv[kc][db] = floatx16{};
         }
 
-    RT qr, dor;
-    CT qtr, dotr;
-    float lse_r = 0.f, d_r = 0.f;   // one query per thread for the first 64 threads
-    auto load_tile = [&](int t) {
-        const int64_t r0 = (int64_t)t * kBN;
-        qr.load(Qh, r0, S);
-        dor.load(dOh, r0, S);
-        qtr.load(QTh, r0, a.S_pad);
-        dotr.load(dOTh, r0, a.S_pad);
-        if (threadIdx.x < kBN) {
-            const int64_t q = r0 + threadIdx.x;
-            lse_r = q < S ? LSEh[q] * kLog2e : 0.f;
-            d_r = q < S ? Dh[q] : 0.f;
-        }
-    };
-    auto store_tile = [&](T* b) {
-        qr.store(b);
-        dor.store(b + RSZ);
-        qtr.store(b + 2 * RSZ);
-        dotr.store(b + 2 * RSZ + CSZ);
-        float* f = reinterpret_cast<float*>(b + 2 * RSZ + 2 * CSZ);
-        if (threadIdx.x < kBN) {
-            f[threadIdx.x] = lse_r;
-            f[kBN + threadIdx.x] = d_r;
+    const int lane_w = threadIdx.x & 63, wave_w = threadIdx.x >> 6;
+    auto stage = [&](int t, unsigned char* b) {
+        auto clamp = [&](int r) {
+            const int64_t row = (int64_t)t * kBN + r;
+            return row < S ? row : S - 1;
+        };
+        stage_tile<RROWB, RBYTES>(b, [&](int r) { return Qh + clamp(r) * D; });
+        stage_tile<RROWB, RBYTES>(b + RBYTES, [&](int r) { return dOh + clamp(r) * D; });
+        stage_tile<CROWB, CBYTES>(b + 2 * RBYTES, [&](int r) { return QTh + r * a.S_pad + (int64_t)t * kBN; });
+        stage_tile<CROWB, CBYTES>(b + 2 * RBYTES + CBYTES,
+                                  [&](int r) { return dOTh + r * a.S_pad + (int64_t)t * kBN; });
+        // the tile's 64 log-sum-exps (wave 0) and D values (wave 1), 4 bytes per lane
+        if (wave_w < 2) {
+            const float* src = (wave_w == 0 ? LSEh : Dh) + clamp(lane_w);
+            __builtin_amdgcn_global_load_lds(src, (lds_void*)(b + OFF_F + wave_w * kBN * 4), 4, 0, 0);
         }
     };
 
-    if (t0 < ntiles_total) {
-        load_tile(t0);
-        store_tile(lds);
-    }
-    __syncthreads();
+    if (t0 < ntiles_total) stage(t0, smem);
+    wait_tiles_and_sync();
 
     for (int t = t0; t < ntiles_total; ++t) {
         const int buf = (t - t0) & 1;
-        if (t + 1 < ntiles_total) load_tile(t + 1);
-        const T* lq = lds + buf * BUF;
-        const T* ldo = lq + RSZ;
-        const T* lqt = lq + 2 * RSZ;
-        const T* ldot = lqt + CSZ;
-        const float* lf = reinterpret_cast<const float*>(lqt + 2 * CSZ);
+        if (t + 1 < ntiles_total) stage(t + 1, smem + (buf ^ 1) * BUF);
+        const unsigned char* lq = smem + buf * BUF;
+        const unsigned char* ldo = lq + RBYTES;
+        const unsigned char* lqt = lq + 2 * RBYTES;
+        const unsigned char* ldot = lqt + CBYTES;
+        const float* lf = reinterpret_cast<const float*>(lq + OFF_F);
 #pragma unroll
         for (int qs = 0; qs < 2; ++qs) {
             const int64_t q0 = (int64_t)t * kBN + 32 * qs;
@@ -521,8 +491,8 @@ __global__ __launch_bounds__(kThreads) void attn_dkdv_kernel(const T* __restrict
             F qa[D / 16], da[D / 16];
 #pragma unroll
             for (int cc = 0; cc < D / 16; ++cc) {
-                qa[cc] = load8(lq + (32 * qs + col) * RT::LD + 16 * cc + 8 * h);
-                da[cc] = load8(ldo + (32 * qs + col) * RT::LD + 16 * cc + 8 * h);
+                qa[cc] = tile_frag<T, RROWB>(lq, 32 * qs + col, 16 * cc + 8 * h);
+                da[cc] = tile_frag<T, RROWB>(ldo, 32 * qs + col, 16 * cc + 8 * h);
             }
             float lrow[16], drow[16];
 #pragma unroll
@@ -531,7 +501,7 @@ __global__ __launch_bounds__(kThreads) void attn_dkdv_kernel(const T* __restrict
                 const floatx4 d4 = *reinterpret_cast<const floatx4*>(lf + kBN + 32 * qs + 8 * m + 4 * h);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    lrow[4 * m + i] = l4[i];
+                    lrow[4 * m + i] = -l4[i] * kLog2e;
                     drow[4 * m + i] = d4[i];
                 }
             }
@@ -553,7 +523,7 @@ __global__ __launch_bounds__(kThreads) void attn_dkdv_kernel(const T* __restrict
                 }
 #pragma unroll
                 for (int j = 0; j < 16; ++j) {
-                    const float pv = fast_exp2(fmaf(sp[j], a.scale_log2, -lrow[j]));
+                    const float pv = fast_exp2(fmaf(sp[j], a.scale_log2, lrow[j]));
                     sp[j] = pv;
                     dp[j] = pv * (dp[j] - drow[j]);
                 }
@@ -564,8 +534,8 @@ __global__ __launch_bounds__(kThreads) void attn_dkdv_kernel(const T* __restrict
                     split_frag<T>(dp, c2, gh, gl);
 #pragma unroll
                     for (int db = 0; db < D / 32; ++db) {
-                        const F dof = load_4_4(ldot + (32 * db + col) * CT::LD + 32 * qs + 16 * c2 + 4 * h);
-                        const F qtf = load_4_4(lqt + (32 * db + col) * CT::LD + 32 * qs + 16 * c2 + 4 * h);
+                        const F dof = tile_frag<T, CROWB>(ldot, 32 * db + col, 32 * qs + 16 * c2 + 8 * h);
+                        const F qtf = tile_frag<T, CROWB>(lqt, 32 * db + col, 32 * qs + 16 * c2 + 8 * h);
                         mma_k16(dv[kc][db], dof, ph);
                         mma_k16(dk[kc][db], qtf, gh);
                         if (kSplitP<T>) {
@@ -576,8 +546,7 @@ __global__ __launch_bounds__(kThreads) void attn_dkdv_kernel(const T* __restrict
                 }
             }
         }
-        if (t + 1 < ntiles_total) store_tile(lds + (buf ^ 1) * BUF);
-        __syncthreads();
+        wait_tiles_and_sync();
     }
 
 #pragma unroll
@@ -599,13 +568,11 @@ __global__ __launch_bounds__(kThreads) void attn_dkdv_kernel(const T* __restrict
 }
 
 template <typename T, int D>
-size_t fwd_lds() { return 2 * (kBN * RowTile<T, D>::LD + D * ColTile<T, D>::LD) * sizeof(T); }
+size_t fwd_lds() { return 2 * 2 * kBN * D * sizeof(T); }
 template <typename T, int D>
-size_t dq_lds() { return 2 * (2 * kBN * RowTile<T, D>::LD + D * ColTile<T, D>::LD) * sizeof(T); }
+size_t dq_lds() { return 2 * 3 * kBN * D * sizeof(T); }
 template <typename T, int D>
-size_t dkdv_lds() {
-    return 2 * ((2 * kBN * RowTile<T, D>::LD + 2 * D * ColTile<T, D>::LD) * sizeof(T) + 2 * kBN * sizeof(float));
-}
+size_t dkdv_lds() { return 2 * (4 * kBN * D * sizeof(T) + 2 * kBN * sizeof(float)); }
 
 AttnK make_k(const AttnArgs& a) {
     AttnK k{};

@@ -36,7 +36,13 @@ __device__ __forceinline__ int level_of(const MapGeo& G, int64_t flat) {
 }
 
 // Write the [kRows x d] tile held in LDS (row stride d + pad) as columns
-// s0 .. s0+63 of the transposed array xT [d][S_pad].
+// s0 .. s0+63 of the transposed array xT [d][S_pad].  Within every aligned
+// group of 16 columns the order is 0-3, 8-11, 4-7, 12-15 (bits 2 and 3 of the
+// column swapped): that is the k order in which the attention kernels feed a
+// C tile back into the matrix cores, so each lane reads its 8 keys as one
+// contiguous 16-byte run.
+__device__ __forceinline__ int key_perm16(int p) { return (p & ~12) | ((p >> 1) & 4) | ((p << 1) & 8); }
+
 template <typename T>
 __device__ __forceinline__ void store_transposed(const T* tile, int ld, int64_t d, T* xT, int64_t S_pad,
                                                  int64_t s0) {
@@ -47,7 +53,7 @@ __device__ __forceinline__ void store_transposed(const T* tile, int ld, int64_t 
         const int dim = task / per_row, cv = task - dim * per_row;
         VT out;
 #pragma unroll
-        for (int i = 0; i < VEC; ++i) out[i] = tile[(cv * VEC + i) * ld + dim];
+        for (int i = 0; i < VEC; ++i) out[i] = tile[key_perm16(cv * VEC + i) * ld + dim];
         *reinterpret_cast<VT*>(xT + dim * S_pad + s0 + cv * VEC) = out;
     }
 }
