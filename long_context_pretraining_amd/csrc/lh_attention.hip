@@ -30,6 +30,7 @@ constexpr int kWaveRows = 64;   // queries (fwd, dQ) or keys (dK/dV) per wave
 constexpr int kBlockRows = 4 * kWaveRows;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr int kDkdvKC = 1;      // 32-key column blocks per dK/dV wave (1: 8 waves of 32 keys per block)
 
 struct AttnK {
     int64_t BH, S, S_pad;
@@ -54,13 +55,14 @@ typedef __attribute__((address_space(3))) void lds_void;
 template <int ROWB>
 __device__ __forceinline__ int swz(int row, int chunk) { return row * ROWB + ((chunk ^ (row & 7)) << 4); }
 
-template <int ROWB, int BYTES, class RowPtr>
+template <int ROWB, int BYTES, class RowPtr, int NW = 4>
 __device__ __forceinline__ void stage_tile(unsigned char* tile, RowPtr row_ptr) {
-    static_assert(BYTES % 4096 == 0, "tile must split into 1 KB wave instructions");
+    static_assert(BYTES % (1024 * NW) == 0, "tile must split into 1 KB wave instructions");
+    constexpr int PER_WAVE = BYTES / (1024 * NW);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
-    for (int i = 0; i < BYTES / 4096; ++i) {
-        const int base = (wave * (BYTES / 4096) + i) * 1024;
+    for (int i = 0; i < PER_WAVE; ++i) {
+        const int base = (wave * PER_WAVE + i) * 1024;
         const int pos = base + 16 * lane;
         const int row = pos / ROWB;
         const int chunk = ((pos % ROWB) >> 4) ^ (row & 7);
@@ -404,8 +406,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_dq_kernel(const T* __restric
 // S = Q K^T, P = exp(S - LSE), dP = dO V^T, dS = P (dP - D),
 // dV^T += dO^T P, dK^T += Q^T dS  (P and dS as bf16 hi + lo parts).
 // ---------------------------------------------------------------------------
-template <typename T, int D, typename OutT>
-__global__ __launch_bounds__(kThreads) void attn_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K,
+template <typename T, int D, typename OutT, int KC>
+__global__ __launch_bounds__(64 * (8 / KC)) void attn_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K,
                                                              const T* __restrict__ V, const T* __restrict__ QT,
                                                              const T* __restrict__ dO, const T* __restrict__ dOT,
                                                              const float* __restrict__ LSE,
@@ -415,6 +417,7 @@ __global__ __launch_bounds__(kThreads) void attn_dkdv_kernel(const T* __restrict
     constexpr int RROWB = D * (int)sizeof(T), CROWB = kBN * (int)sizeof(T);
     constexpr int RBYTES = kBN * RROWB, CBYTES = D * CROWB;
     constexpr int OFF_F = 2 * RBYTES + 2 * CBYTES, BUF = OFF_F + 2 * kBN * 4;
+    constexpr int NW = 8 / KC;                 // waves per block; each owns 32*KC keys, 256 per block
     extern __shared__ __align__(16) unsigned char smem[];
 
     int64_t bh; int kb;
@@ -432,13 +435,13 @@ __global__ __launch_bounds__(kThreads) void attn_dkdv_kernel(const T* __restrict
     const float* Dh = Dv + bh * S;
 
     const int64_t k_blk0 = (int64_t)kb * kBlockRows;
-    const int64_t k_base = k_blk0 + wave * kWaveRows;
+    const int64_t k_base = k_blk0 + wave * 32 * KC;
     const int t0 = (int)(k_blk0 / kBN);
     const int ntiles_total = (int)((S + kBN - 1) / kBN);
 
-    F kf[2][D / 16], vf[2][D / 16];
+    F kf[KC][D / 16], vf[KC][D / 16];
 #pragma unroll
-    for (int kc = 0; kc < 2; ++kc) {
+    for (int kc = 0; kc < KC; ++kc) {
         const int64_t key = k_base + 32 * kc + col;
 #pragma unroll
         for (int c = 0; c < D / 16; ++c) {
@@ -446,9 +449,9 @@ __global__ __launch_bounds__(kThreads) void attn_dkdv_kernel(const T* __restrict
             vf[kc][c] = load8_or_zero(Vh + key * D + 16 * c + 8 * h, key < S);
         }
     }
-    floatx16 dk[2][D / 32], dv[2][D / 32];
+    floatx16 dk[KC][D / 32], dv[KC][D / 32];
 #pragma unroll
-    for (int kc = 0; kc < 2; ++kc)
+    for (int kc = 0; kc < KC; ++kc)
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) {
             dk[kc][db] = floatx16{};
@@ -461,11 +464,14 @@ __global__ __launch_bounds__(kThreads) void attn_dkdv_kernel(const T* __restrict
             const int64_t row = (int64_t)t * kBN + r;
             return row < S ? row : S - 1;
         };
-        stage_tile<RROWB, RBYTES>(b, [&](int r) { return Qh + clamp(r) * D; });
-        stage_tile<RROWB, RBYTES>(b + RBYTES, [&](int r) { return dOh + clamp(r) * D; });
-        stage_tile<CROWB, CBYTES>(b + 2 * RBYTES, [&](int r) { return QTh + r * a.S_pad + (int64_t)t * kBN; });
-        stage_tile<CROWB, CBYTES>(b + 2 * RBYTES + CBYTES,
-                                  [&](int r) { return dOTh + r * a.S_pad + (int64_t)t * kBN; });
+        auto qrow = [&](int r) { return Qh + clamp(r) * D; };
+        auto dorow = [&](int r) { return dOh + clamp(r) * D; };
+        auto qtrow = [&](int r) { return QTh + r * a.S_pad + (int64_t)t * kBN; };
+        auto dotrow = [&](int r) { return dOTh + r * a.S_pad + (int64_t)t * kBN; };
+        stage_tile<RROWB, RBYTES, decltype(qrow), NW>(b, qrow);
+        stage_tile<RROWB, RBYTES, decltype(dorow), NW>(b + RBYTES, dorow);
+        stage_tile<CROWB, CBYTES, decltype(qtrow), NW>(b + 2 * RBYTES, qtrow);
+        stage_tile<CROWB, CBYTES, decltype(dotrow), NW>(b + 2 * RBYTES + CBYTES, dotrow);
         // the tile's 64 log-sum-exps (wave 0) and D values (wave 1), 4 bytes per lane
         if (wave_w < 2) {
             const float* src = (wave_w == 0 ? LSEh : Dh) + clamp(lane_w);
@@ -506,7 +512,7 @@ __global__ __launch_bounds__(kThreads) void attn_dkdv_kernel(const T* __restrict
                 }
             }
 #pragma unroll
-            for (int kc = 0; kc < 2; ++kc) {
+            for (int kc = 0; kc < KC; ++kc) {
                 floatx16 sp = floatx16{}, dp = floatx16{};
 #pragma unroll
                 for (int cc = 0; cc < D / 16; ++cc) {
@@ -550,7 +556,7 @@ __global__ __launch_bounds__(kThreads) void attn_dkdv_kernel(const T* __restrict
     }
 
 #pragma unroll
-    for (int kc = 0; kc < 2; ++kc) {
+    for (int kc = 0; kc < KC; ++kc) {
         const int64_t key = k_base + 32 * kc + col;
         if (key >= S) continue;
         OutT* rk = dK + (bh * S + key) * D;
@@ -599,10 +605,10 @@ hipError_t dkdv_t(const AttnArgs& a, const void* Q, const void* K, const void* V
                   const void* dOT, const float* lse, const float* Dv, void* dK, void* dV, hipStream_t st) {
     const AttnK k = make_k(a);
     const size_t sh = dkdv_lds<T, D>();
-    static const hipError_t attr = hipFuncSetAttribute((const void*)attn_dkdv_kernel<T, D, OutT>,
+    static const hipError_t attr = hipFuncSetAttribute((const void*)attn_dkdv_kernel<T, D, OutT, kDkdvKC>,
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)sh);
     (void)attr;
-    attn_dkdv_kernel<T, D, OutT><<<dim3((unsigned)(k.nblk * a.BH)), kThreads, sh, st>>>(
+    attn_dkdv_kernel<T, D, OutT, kDkdvKC><<<dim3((unsigned)(k.nblk * a.BH)), 64 * (8 / kDkdvKC), sh, st>>>(
         (const T*)Q, (const T*)K, (const T*)V, (const T*)QT, (const T*)dO, (const T*)dOT, lse, Dv, (OutT*)dK,
         (OutT*)dV, k);
     return hipGetLastError();
