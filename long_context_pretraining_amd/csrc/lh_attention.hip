@@ -41,9 +41,11 @@ struct AttnK {
 // ---------------------------------------------------------------------------
 // LDS tiles.  A tile is ROWS rows of ROWB bytes, filled straight from global
 // memory by global_load_lds (16 bytes per lane, 1 KB per wave instruction, no
-// staging registers).  16-byte chunk c of row r sits at chunk c ^ (r & 7) of
-// that row, so the 8 lanes of one LDS phase that read the same chunk of 8
-// consecutive rows hit 8 different bank groups.
+// staging registers).  16-byte chunk c of row r sits at chunk c ^ f(r) of that
+// row, with f(r) = (r ^ (r >> 3)) & 7 for 128-byte rows and r & 15 for
+// 256-byte rows: lanes reading the same chunk of 8 consecutive rows then hit
+// 8 different 16-byte bank groups of a 128-byte bank window, and 16
+// consecutive rows 16 different groups of a 256-byte window.
 // Row tiles hold 64 rows of a row-major [S][D] array (rows past S repeat row
 // S-1; the masks make them irrelevant).  Column tiles hold D rows of a
 // transposed [D][S_pad] array, 64 keys each, in the slot order the gather and
@@ -53,7 +55,11 @@ struct AttnK {
 typedef __attribute__((address_space(3))) void lds_void;
 
 template <int ROWB>
-__device__ __forceinline__ int swz(int row, int chunk) { return row * ROWB + ((chunk ^ (row & 7)) << 4); }
+__device__ __forceinline__ int swz_key(int row) {
+    return ROWB == 128 ? ((row ^ (row >> 3)) & 7) : (row & 15);
+}
+template <int ROWB>
+__device__ __forceinline__ int swz(int row, int chunk) { return row * ROWB + ((chunk ^ swz_key<ROWB>(row)) << 4); }
 
 template <int ROWB, int BYTES, class RowPtr, int NW = 4>
 __device__ __forceinline__ void stage_tile(unsigned char* tile, RowPtr row_ptr) {
@@ -65,7 +71,7 @@ __device__ __forceinline__ void stage_tile(unsigned char* tile, RowPtr row_ptr) 
         const int base = (wave * PER_WAVE + i) * 1024;
         const int pos = base + 16 * lane;
         const int row = pos / ROWB;
-        const int chunk = ((pos % ROWB) >> 4) ^ (row & 7);
+        const int chunk = ((pos % ROWB) >> 4) ^ swz_key<ROWB>(row);
         const unsigned char* g = reinterpret_cast<const unsigned char*>(row_ptr(row)) + (chunk << 4);
         __builtin_amdgcn_global_load_lds(g, (lds_void*)(tile + base), 16, 0, 0);
     }
@@ -175,59 +181,77 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const T* __restri
         if (t + 1 < ntiles) stage(t + 1, smem + (buf ^ 1) * BUF);
         const unsigned char* lk = smem + buf * BUF;
         const unsigned char* lv = lk + KBYTES;
+        const int kt0 = t * kBN;
+        if (kt0 <= q_last_w) {   // this wave sees at least one key of the tile
+            // S^T for both 32-key halves of the tile, then one max/rescale per 64 keys
+            floatx16 s[2][2];
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            const int kbase = t * kBN + 32 * ks;
-            if (kbase > q_last_w) continue;
-            floatx16 s[2] = {floatx16{}, floatx16{}};
+            for (int ks = 0; ks < 2; ++ks) {
+                s[ks][0] = floatx16{};
+                s[ks][1] = floatx16{};
 #pragma unroll
-            for (int cc = 0; cc < D / 16; ++cc) {
-                const F kf = tile_frag<T, KROWB>(lk, 32 * ks + col, 16 * cc + 8 * h);
-                mma_k16(s[0], kf, qf[0][cc]);
-                mma_k16(s[1], kf, qf[1][cc]);
-            }
-            if (kbase + 31 > q_base || kbase + 31 >= S) {   // diagonal or tail: mask key > query / key >= S
-                const int l0 = q_lim0 - kbase, l1 = q_lim1 - kbase;
-#pragma unroll
-                for (int j = 0; j < 16; ++j) {
-                    if (c_row0(j) > l0) s[0][j] = -INFINITY;
-                    if (c_row0(j) > l1) s[1][j] = -INFINITY;
+                for (int cc = 0; cc < D / 16; ++cc) {
+                    const F kf = tile_frag<T, KROWB>(lk, 32 * ks + col, 16 * cc + 8 * h);
+                    mma_k16(s[ks][0], kf, qf[0][cc]);
+                    mma_k16(s[ks][1], kf, qf[1][cc]);
                 }
             }
+            if (kt0 + kBN - 1 > q_base || kt0 + kBN - 1 >= S) {   // diagonal or tail: key > query / key >= S
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+                    const int l0 = q_lim0 - kt0 - 32 * ks, l1 = q_lim1 - kt0 - 32 * ks;
+#pragma unroll
+                    for (int j = 0; j < 16; ++j) {
+                        if (c_row0(j) > l0) s[ks][0][j] = -INFINITY;
+                        if (c_row0(j) > l1) s[ks][1][j] = -INFINITY;
+                    }
+                }
+            }
+            float neg[2];
 #pragma unroll
             for (int cb = 0; cb < 2; ++cb) {
-                const float mx = max_halves(max16(s[cb])) * c;
-                if (wave_any(mx > m_i[cb] + 8.f)) {
-                    const float m_new = fmaxf(m_i[cb], mx);
-                    const float alpha = m_new == m_i[cb] ? 1.f : fast_exp2(m_i[cb] - m_new);
+                const float mx = max_halves(__builtin_fmaxf(max16(s[0][cb]), max16(s[1][cb]))) * c;
+                // Each query moves its own reference only when its own max grew by more
+                // than 2^8 (others scale by exactly 1), so a query's result never depends
+                // on the other queries of the wave.
+                const bool need = mx > m_i[cb] + 8.f;
+                if (wave_any(need)) {
+                    const float m_new = need ? mx : m_i[cb];
+                    const float alpha = need ? fast_exp2(m_i[cb] - m_new) : 1.f;
                     m_i[cb] = m_new;
                     l_i[cb] *= alpha;
 #pragma unroll
                     for (int db = 0; db < D / 32; ++db) o[cb][db] *= alpha;
                 }
-                const float neg = m_i[cb] == -INFINITY ? 0.f : -m_i[cb];
-                float rs = 0.f;
-#pragma unroll
-                for (int j = 0; j < 16; ++j) {
-                    const float pv = fast_exp2(fmaf(s[cb][j], c, neg));
-                    s[cb][j] = pv;
-                    rs += pv;
-                }
-                l_i[cb] += rs;
+                neg[cb] = m_i[cb] == -INFINITY ? 0.f : -m_i[cb];
             }
 #pragma unroll
-            for (int c2 = 0; c2 < 2; ++c2) {
-                F p0, p1, r0, r1;
-                split_frag<T>(s[0], c2, p0, r0);
-                split_frag<T>(s[1], c2, p1, r1);
+            for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
-                for (int db = 0; db < D / 32; ++db) {
-                    const F vf = tile_frag<T, VROWB>(lv, 32 * db + col, 32 * ks + 16 * c2 + 8 * h);
-                    mma_k16(o[0][db], vf, p0);
-                    mma_k16(o[1][db], vf, p1);
-                    if (kSplitP<T>) {
-                        mma_k16(o[0][db], vf, r0);
-                        mma_k16(o[1][db], vf, r1);
+                for (int cb = 0; cb < 2; ++cb) {
+                    float rs = 0.f;
+#pragma unroll
+                    for (int j = 0; j < 16; ++j) {
+                        const float pv = fast_exp2(fmaf(s[ks][cb][j], c, neg[cb]));
+                        s[ks][cb][j] = pv;
+                        rs += pv;
+                    }
+                    l_i[cb] += rs;
+                }
+#pragma unroll
+                for (int c2 = 0; c2 < 2; ++c2) {
+                    F p0, p1, r0, r1;
+                    split_frag<T>(s[ks][0], c2, p0, r0);
+                    split_frag<T>(s[ks][1], c2, p1, r1);
+#pragma unroll
+                    for (int db = 0; db < D / 32; ++db) {
+                        const F vf = tile_frag<T, VROWB>(lv, 32 * db + col, 32 * ks + 16 * c2 + 8 * h);
+                        mma_k16(o[0][db], vf, p0);
+                        mma_k16(o[1][db], vf, p1);
+                        if (kSplitP<T>) {
+                            mma_k16(o[0][db], vf, r0);
+                            mma_k16(o[1][db], vf, r1);
+                        }
                     }
                 }
             }
