@@ -30,7 +30,8 @@ constexpr int kWaveRows = 64;   // queries (fwd, dQ) or keys (dK/dV) per wave
 constexpr int kBlockRows = 4 * kWaveRows;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr int kDkdvKC = 1;      // 32-key column blocks per dK/dV wave (1: 8 waves of 32 keys per block)
+constexpr int kDkdvKC = 1;      // 32-key column blocks per dK/dV wave
+constexpr int kDkdvNW = 8;      // waves per dK/dV block (blocks of 32 * KC * NW keys)
 
 struct AttnK {
     int64_t BH, S, S_pad;
@@ -430,8 +431,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_dq_kernel(const T* __restric
 // S = Q K^T, P = exp(S - LSE), dP = dO V^T, dS = P (dP - D),
 // dV^T += dO^T P, dK^T += Q^T dS  (P and dS as bf16 hi + lo parts).
 // ---------------------------------------------------------------------------
-template <typename T, int D, typename OutT, int KC>
-__global__ __launch_bounds__(64 * (8 / KC)) void attn_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K,
+template <typename T, int D, typename OutT, int KC, int NW>
+__global__ __launch_bounds__(64 * NW, 8 / NW) void attn_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K,
                                                              const T* __restrict__ V, const T* __restrict__ QT,
                                                              const T* __restrict__ dO, const T* __restrict__ dOT,
                                                              const float* __restrict__ LSE,
@@ -441,7 +442,7 @@ __global__ __launch_bounds__(64 * (8 / KC)) void attn_dkdv_kernel(const T* __res
     constexpr int RROWB = D * (int)sizeof(T), CROWB = kBN * (int)sizeof(T);
     constexpr int RBYTES = kBN * RROWB, CBYTES = D * CROWB;
     constexpr int OFF_F = 2 * RBYTES + 2 * CBYTES, BUF = OFF_F + 2 * kBN * 4;
-    constexpr int NW = 8 / KC;                 // waves per block; each owns 32*KC keys, 256 per block
+    constexpr int BK = 32 * KC * NW;           // keys per block: NW waves of 32*KC keys
     extern __shared__ __align__(16) unsigned char smem[];
 
     int64_t bh; int kb;
@@ -458,7 +459,7 @@ __global__ __launch_bounds__(64 * (8 / KC)) void attn_dkdv_kernel(const T* __res
     const float* LSEh = LSE + bh * S;
     const float* Dh = Dv + bh * S;
 
-    const int64_t k_blk0 = (int64_t)kb * kBlockRows;
+    const int64_t k_blk0 = (int64_t)kb * BK;
     const int64_t k_base = k_blk0 + wave * 32 * KC;
     const int t0 = (int)(k_blk0 / kBN);
     const int ntiles_total = (int)((S + kBN - 1) / kBN);
@@ -514,63 +515,78 @@ __global__ __launch_bounds__(64 * (8 / KC)) void attn_dkdv_kernel(const T* __res
         const unsigned char* lqt = lq + 2 * RBYTES;
         const unsigned char* ldot = lqt + CBYTES;
         const float* lf = reinterpret_cast<const float*>(lq + OFF_F);
+        const int64_t qt0 = (int64_t)t * kBN;
+        if (k_base <= qt0 + kBN - 1 && k_base < S) {   // some key of this wave precedes some query of the tile
+            // S = Q K^T and dP = dO V^T for both 32-query halves first
+            floatx16 sp[2][KC], dp[2][KC];
 #pragma unroll
-        for (int qs = 0; qs < 2; ++qs) {
-            const int64_t q0 = (int64_t)t * kBN + 32 * qs;
-            if (k_base > q0 + 31 || k_base >= S) continue;   // every key of this wave after every query
-            F qa[D / 16], da[D / 16];
-#pragma unroll
-            for (int cc = 0; cc < D / 16; ++cc) {
-                qa[cc] = tile_frag<T, RROWB>(lq, 32 * qs + col, 16 * cc + 8 * h);
-                da[cc] = tile_frag<T, RROWB>(ldo, 32 * qs + col, 16 * cc + 8 * h);
-            }
-            float lrow[16], drow[16];
-#pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                const floatx4 l4 = *reinterpret_cast<const floatx4*>(lf + 32 * qs + 8 * m + 4 * h);
-                const floatx4 d4 = *reinterpret_cast<const floatx4*>(lf + kBN + 32 * qs + 8 * m + 4 * h);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    lrow[4 * m + i] = -l4[i] * kLog2e;
-                    drow[4 * m + i] = d4[i];
-                }
-            }
-#pragma unroll
-            for (int kc = 0; kc < KC; ++kc) {
-                floatx16 sp = floatx16{}, dp = floatx16{};
+            for (int qs = 0; qs < 2; ++qs) {
+                F qa[D / 16], da[D / 16];
 #pragma unroll
                 for (int cc = 0; cc < D / 16; ++cc) {
-                    mma_k16(sp, qa[cc], kf[kc][cc]);
-                    mma_k16(dp, da[cc], vf[kc][cc]);
-                }
-                if (k_base + 32 * kc + 31 > q0 || q0 + 31 >= S) {   // diagonal or tail
-                    // row j (query q0 + 4h + c_row0(j)) is masked when the key is after it or it is past S
-                    const int kl = (int)(k_base + 32 * kc + col - q0) - 4 * h;
-                    const int sl = (int)(S - q0) - 4 * h;
-#pragma unroll
-                    for (int j = 0; j < 16; ++j)
-                        if (c_row0(j) < kl || c_row0(j) >= sl) sp[j] = -INFINITY;
+                    qa[cc] = tile_frag<T, RROWB>(lq, 32 * qs + col, 16 * cc + 8 * h);
+                    da[cc] = tile_frag<T, RROWB>(ldo, 32 * qs + col, 16 * cc + 8 * h);
                 }
 #pragma unroll
-                for (int j = 0; j < 16; ++j) {
-                    const float pv = fast_exp2(fmaf(sp[j], a.scale_log2, lrow[j]));
-                    sp[j] = pv;
-                    dp[j] = pv * (dp[j] - drow[j]);
+                for (int kc = 0; kc < KC; ++kc) {
+                    sp[qs][kc] = floatx16{};
+                    dp[qs][kc] = floatx16{};
+#pragma unroll
+                    for (int cc = 0; cc < D / 16; ++cc) {
+                        mma_k16(sp[qs][kc], qa[cc], kf[kc][cc]);
+                        mma_k16(dp[qs][kc], da[cc], vf[kc][cc]);
+                    }
+                }
+            }
+            if (k_base + 32 * KC - 1 > qt0 || qt0 + kBN - 1 >= S) {   // diagonal or tail
+#pragma unroll
+                for (int qs = 0; qs < 2; ++qs)
+#pragma unroll
+                    for (int kc = 0; kc < KC; ++kc) {
+                        // row j (query qt0 + 32qs + 4h + c_row0(j)) is masked when the key is after it or it is past S
+                        const int kl = (int)(k_base + 32 * kc + col - qt0) - 32 * qs - 4 * h;
+                        const int sl = (int)(S - qt0) - 32 * qs - 4 * h;
+#pragma unroll
+                        for (int j = 0; j < 16; ++j)
+                            if (c_row0(j) < kl || c_row0(j) >= sl) sp[qs][kc][j] = -INFINITY;
+                    }
+            }
+#pragma unroll
+            for (int qs = 0; qs < 2; ++qs) {
+                float lrow[16], drow[16];
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    const floatx4 l4 = *reinterpret_cast<const floatx4*>(lf + 32 * qs + 8 * m + 4 * h);
+                    const floatx4 d4 = *reinterpret_cast<const floatx4*>(lf + kBN + 32 * qs + 8 * m + 4 * h);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        lrow[4 * m + i] = -l4[i] * kLog2e;
+                        drow[4 * m + i] = d4[i];
+                    }
                 }
 #pragma unroll
-                for (int c2 = 0; c2 < 2; ++c2) {
-                    F ph, pl, gh, gl;
-                    split_frag<T>(sp, c2, ph, pl);
-                    split_frag<T>(dp, c2, gh, gl);
+                for (int kc = 0; kc < KC; ++kc) {
 #pragma unroll
-                    for (int db = 0; db < D / 32; ++db) {
-                        const F dof = tile_frag<T, CROWB>(ldot, 32 * db + col, 32 * qs + 16 * c2 + 8 * h);
-                        const F qtf = tile_frag<T, CROWB>(lqt, 32 * db + col, 32 * qs + 16 * c2 + 8 * h);
-                        mma_k16(dv[kc][db], dof, ph);
-                        mma_k16(dk[kc][db], qtf, gh);
-                        if (kSplitP<T>) {
-                            mma_k16(dv[kc][db], dof, pl);
-                            mma_k16(dk[kc][db], qtf, gl);
+                    for (int j = 0; j < 16; ++j) {
+                        const float pv = fast_exp2(fmaf(sp[qs][kc][j], a.scale_log2, lrow[j]));
+                        sp[qs][kc][j] = pv;
+                        dp[qs][kc][j] = pv * (dp[qs][kc][j] - drow[j]);
+                    }
+#pragma unroll
+                    for (int c2 = 0; c2 < 2; ++c2) {
+                        F ph, pl, gh, gl;
+                        split_frag<T>(sp[qs][kc], c2, ph, pl);
+                        split_frag<T>(dp[qs][kc], c2, gh, gl);
+#pragma unroll
+                        for (int db = 0; db < D / 32; ++db) {
+                            const F dof = tile_frag<T, CROWB>(ldot, 32 * db + col, 32 * qs + 16 * c2 + 8 * h);
+                            const F qtf = tile_frag<T, CROWB>(lqt, 32 * db + col, 32 * qs + 16 * c2 + 8 * h);
+                            mma_k16(dv[kc][db], dof, ph);
+                            mma_k16(dk[kc][db], qtf, gh);
+                            if (kSplitP<T>) {
+                                mma_k16(dv[kc][db], dof, pl);
+                                mma_k16(dk[kc][db], qtf, gl);
+                            }
                         }
                     }
                 }
@@ -629,12 +645,15 @@ hipError_t dkdv_t(const AttnArgs& a, const void* Q, const void* K, const void* V
                   const void* dOT, const float* lse, const float* Dv, void* dK, void* dV, hipStream_t st) {
     const AttnK k = make_k(a);
     const size_t sh = dkdv_lds<T, D>();
-    static const hipError_t attr = hipFuncSetAttribute((const void*)attn_dkdv_kernel<T, D, OutT, kDkdvKC>,
+    constexpr int BK = 32 * kDkdvKC * kDkdvNW;
+    AttnK kk = k;
+    kk.nblk = (int)((a.S + BK - 1) / BK);
+    static const hipError_t attr = hipFuncSetAttribute((const void*)attn_dkdv_kernel<T, D, OutT, kDkdvKC, kDkdvNW>,
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)sh);
     (void)attr;
-    attn_dkdv_kernel<T, D, OutT, kDkdvKC><<<dim3((unsigned)(k.nblk * a.BH)), 64 * (8 / kDkdvKC), sh, st>>>(
+    attn_dkdv_kernel<T, D, OutT, kDkdvKC, kDkdvNW><<<dim3((unsigned)(kk.nblk * a.BH)), 64 * kDkdvNW, sh, st>>>(
         (const T*)Q, (const T*)K, (const T*)V, (const T*)QT, (const T*)dO, (const T*)dOT, lse, Dv, (OutT*)dK,
-        (OutT*)dV, k);
+        (OutT*)dV, kk);
     return hipGetLastError();
 }
 
