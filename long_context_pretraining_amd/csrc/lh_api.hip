@@ -69,13 +69,13 @@ lh_status plan_impl(const lh_desc* d, lh_plan* out, LhGeom* g) {
     for (int i = 0; i < 8; ++i) { P.fwd_off[i] = o; o += align_up(fwd_sizes[i]); }
     P.fwd_ws_bytes = o;
     o = 0;
-    const size_t bwd_sizes[6] = {row, colT, vec, rowf, rowf, rowf};
-    for (int i = 0; i < 6; ++i) { P.bwd_off[i] = o; o += align_up(bwd_sizes[i]); }
+    const size_t bwd_sizes[7] = {row, colT, vec, rowf, rowf, rowf, vec};
+    for (int i = 0; i < 7; ++i) { P.bwd_off[i] = o; o += align_up(bwd_sizes[i]); }
     P.bwd_ws_bytes = o;
     const int64_t N_pad = round64(d->N);
     const size_t dT = (size_t)BH * d->d * N_pad * e;
     P.dense_fwd_ws_bytes = align_up(dT) + align_up((size_t)BH * d->N * d->d * 4);
-    P.dense_bwd_ws_bytes = 3 * align_up(dT) + align_up((size_t)BH * d->N * 4);
+    P.dense_bwd_ws_bytes = 3 * align_up(dT) + 2 * align_up((size_t)BH * d->N * 4);
 
     *out = P;
     if (g) {
@@ -207,10 +207,11 @@ lh_status lh_backward(const lh_desc* desc, const int32_t* gidx, const int32_t* g
     void* dog = at(bwd_ws, P.bwd_off[LH_BWD_DO]);
     void* dogT = at(bwd_ws, P.bwd_off[LH_BWD_DOT]);
     float* Dv = (float*)at(bwd_ws, P.bwd_off[LH_BWD_D]);
+    float* lse2 = (float*)at(bwd_ws, P.bwd_off[LH_BWD_LSE2]);
     float* dxg[3] = {(float*)at(bwd_ws, P.bwd_off[LH_BWD_DQ]), (float*)at(bwd_ws, P.bwd_off[LH_BWD_DK]),
                      (float*)at(bwd_ws, P.bwd_off[LH_BWD_DV])};
     hipError_t e = probed(LH_KERNEL_SCATTER_BWD, st, [&] {
-        return launch_scatter_bwd(g, desc->dtype, dout, og, gidx, dog, dogT, Dv, st);
+        return launch_scatter_bwd(g, desc->dtype, dout, og, gidx, lse, dog, dogT, Dv, lse2, st);
     });
     const void* Qg = at(fwd_ws, P.fwd_off[LH_FWD_QG]);
     const void* Kg = at(fwd_ws, P.fwd_off[LH_FWD_KG]);
@@ -219,11 +220,11 @@ lh_status lh_backward(const lh_desc* desc, const int32_t* gidx, const int32_t* g
     if (e == hipSuccess)
         e = probed(LH_KERNEL_ATTN_DKDV, st, [&] {
             return launch_attn_dkdv(a, desc->dtype, true, Qg, Kg, Vg, at(fwd_ws, P.fwd_off[LH_FWD_QT]), dog, dogT,
-                                    lse, Dv, dxg[1], dxg[2], st);
+                                    lse2, Dv, dxg[1], dxg[2], st);
         });
     if (e == hipSuccess)
         e = probed(LH_KERNEL_ATTN_DQ, st, [&] {
-            return launch_attn_dq(a, desc->dtype, true, Qg, Kg, Vg, at(fwd_ws, P.fwd_off[LH_FWD_KT]), dog, lse, Dv,
+            return launch_attn_dq(a, desc->dtype, true, Qg, Kg, Vg, at(fwd_ws, P.fwd_off[LH_FWD_KT]), dog, lse2, Dv,
                                   dxg[0], st);
         });
     if (e == hipSuccess) {
@@ -273,22 +274,23 @@ lh_status dense_causal_attn_backward(const lh_desc* desc, const void* q, const v
     void* kT = at(ws, dT);
     void* doT = at(ws, 2 * dT);
     float* Dv = (float*)at(ws, 3 * dT);
+    float* lse2 = (float*)at(ws, 3 * dT + align_up((size_t)BH * N * 4));
     const float* o32 = (const float*)at(fwd_ws, dT);
     hipError_t e = launch_transpose(desc->dtype, BH, N, N_pad, desc->d, q, qT, st);
     if (e == hipSuccess) e = launch_transpose(desc->dtype, BH, N, N_pad, desc->d, k, kT, st);
     if (e == hipSuccess)
         e = probed(LH_KERNEL_DENSE_PREP, st, [&] {
-            return launch_dense_bwd_prep(desc->dtype, BH, N, N_pad, desc->d, dout, o32, doT, Dv, st);
+            return launch_dense_bwd_prep(desc->dtype, BH, N, N_pad, desc->d, dout, o32, lse, doT, Dv, lse2, st);
         });
     AttnArgs a{BH, N, N_pad, desc->d, softmax_scale(desc)};
     const bool f32 = desc->dtype == LH_F32;
     if (e == hipSuccess)
         e = probed(LH_KERNEL_ATTN_DKDV, st, [&] {
-            return launch_attn_dkdv(a, desc->dtype, f32, q, k, v, qT, dout, doT, lse, Dv, dk, dv, st);
+            return launch_attn_dkdv(a, desc->dtype, f32, q, k, v, qT, dout, doT, lse2, Dv, dk, dv, st);
         });
     if (e == hipSuccess)
         e = probed(LH_KERNEL_ATTN_DQ, st,
-                   [&] { return launch_attn_dq(a, desc->dtype, f32, q, k, v, kT, dout, lse, Dv, dq, st); });
+                   [&] { return launch_attn_dq(a, desc->dtype, f32, q, k, v, kT, dout, lse2, Dv, dq, st); });
     return dev(e);
 }
 

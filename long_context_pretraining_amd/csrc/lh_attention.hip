@@ -333,7 +333,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_dq_kernel(const T* __restric
             qf[cb][c] = load8_or_zero(Qh + q * D + 16 * c + 8 * h, ok);
             df[cb][c] = load8_or_zero(dOh + q * D + 16 * c + 8 * h, ok);
         }
-        lse2[cb] = ok ? LSE[bh * S + q] * kLog2e : 0.f;
+        lse2[cb] = ok ? LSE[bh * S + q] : 0.f;   // log2 units
         dd[cb] = ok ? Dv[bh * S + q] : 0.f;
     }
     floatx16 acc[2][D / 32];
@@ -560,7 +560,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_dkdv_kernel(const T* __r
                     const floatx4 d4 = *reinterpret_cast<const floatx4*>(lf + kBN + 32 * qs + 8 * m + 4 * h);
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        lrow[4 * m + i] = -l4[i] * kLog2e;
+                        lrow[4 * m + i] = l4[i];   // log2 units
                         drow[4 * m + i] = d4[i];
                     }
                 }
@@ -568,7 +568,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_dkdv_kernel(const T* __r
                 for (int kc = 0; kc < KC; ++kc) {
 #pragma unroll
                     for (int j = 0; j < 16; ++j) {
-                        const float pv = fast_exp2(fmaf(sp[qs][kc][j], a.scale_log2, lrow[j]));
+                        const float pv = fast_exp2(fmaf(sp[qs][kc][j], a.scale_log2, -lrow[j]));
                         sp[qs][kc][j] = pv;
                         dp[qs][kc][j] = pv * (dp[qs][kc][j] - drow[j]);
                     }
