@@ -102,9 +102,12 @@ hipEvent_t g_probe_start = nullptr, g_probe_stop = nullptr;
 template <class F>
 hipError_t probed(int id, hipStream_t st, F&& launch) {
     const bool on = id == g_probe_kernel && g_probe_start && g_probe_stop;
-    if (on) hipEventRecord(g_probe_start, st);
+    if (on) {
+        const hipError_t r = hipEventRecord(g_probe_start, st);
+        if (r != hipSuccess) return r;
+    }
     const hipError_t e = launch();
-    if (on) hipEventRecord(g_probe_stop, st);
+    if (on && e == hipSuccess) return hipEventRecord(g_probe_stop, st);
     return e;
 }
 
