@@ -62,19 +62,24 @@ __device__ __forceinline__ int swz_key(int row) {
 template <int ROWB>
 __device__ __forceinline__ int swz(int row, int chunk) { return row * ROWB + ((chunk ^ swz_key<ROWB>(row)) << 4); }
 
-template <int ROWB, int BYTES, class RowPtr, int NW = 4>
-__device__ __forceinline__ void stage_tile(unsigned char* tile, RowPtr row_ptr) {
+// Loads one tile: chunk (wave * PER + i) * 64 + lane of the tile (byte
+// position pos, tile row r = pos / ROWB) receives global 16-byte chunk
+// (pos % ROWB) / 16 ^ f(r) of row r, found at base + row_off(r).  row_off
+// returns a 32-bit byte offset and base is uniform, so the per-lane address is
+// a single 32-bit value.
+template <int ROWB, int BYTES, int NW, class RowOff>
+__device__ __forceinline__ void stage_tile(unsigned char* tile, const void* base, RowOff row_off) {
     static_assert(BYTES % (1024 * NW) == 0, "tile must split into 1 KB wave instructions");
     constexpr int PER_WAVE = BYTES / (1024 * NW);
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, wave = wave_id();
 #pragma unroll
     for (int i = 0; i < PER_WAVE; ++i) {
-        const int base = (wave * PER_WAVE + i) * 1024;
-        const int pos = base + 16 * lane;
+        const int dst = (wave * PER_WAVE + i) * 1024;
+        const int pos = dst + 16 * lane;
         const int row = pos / ROWB;
-        const int chunk = ((pos % ROWB) >> 4) ^ swz_key<ROWB>(row);
-        const unsigned char* g = reinterpret_cast<const unsigned char*>(row_ptr(row)) + (chunk << 4);
-        __builtin_amdgcn_global_load_lds(g, (lds_void*)(tile + base), 16, 0, 0);
+        const uint32_t chunk = (uint32_t)(((pos % ROWB) >> 4) ^ swz_key<ROWB>(row));
+        const unsigned char* g = reinterpret_cast<const unsigned char*>(base) + (row_off(row) + (chunk << 4));
+        __builtin_amdgcn_global_load_lds(g, (lds_void*)(tile + dst), 16, 0, 0);
     }
 }
 
@@ -134,7 +139,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const T* __restri
 
     int64_t bh; int qb;
     block_order(a, true, bh, qb);
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, wave = wave_id();
     const int col = lane & 31, h = lane >> 5;
     const int64_t S = a.S;
     const T* Qh = Q + bh * S * D;
@@ -167,12 +172,16 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const T* __restri
     const int q_lim0 = (int)((q_base + col < S - 1 ? q_base + col : S - 1) - 4 * h);
     const int q_lim1 = (int)((q_base + 32 + col < S - 1 ? q_base + 32 + col : S - 1) - 4 * h);
 
+    const uint32_t last_row = (uint32_t)(S - 1);
+    const uint32_t col_stride = (uint32_t)(a.S_pad * sizeof(T));
     auto stage = [&](int t, unsigned char* b) {
-        stage_tile<KROWB, KBYTES>(b, [&](int r) {
-            const int64_t row = (int64_t)t * kBN + r;
-            return Kh + (row < S ? row : S - 1) * D;
+        const uint32_t r0 = (uint32_t)t * kBN;
+        stage_tile<KROWB, KBYTES, 4>(b, Kh, [&](int r) {   // rows past S repeat row S - 1
+            const uint32_t row = r0 + r < last_row ? r0 + r : last_row;
+            return row * (uint32_t)KROWB;
         });
-        stage_tile<VROWB, VBYTES>(b + KBYTES, [&](int r) { return VTh + r * a.S_pad + (int64_t)t * kBN; });
+        stage_tile<VROWB, VBYTES, 4>(b + KBYTES, reinterpret_cast<const unsigned char*>(VTh) + (int64_t)t * VROWB,
+                                     [&](int r) { return (uint32_t)r * col_stride; });
     };
     stage(0, smem);
     wait_tiles_and_sync();
@@ -198,6 +207,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const T* __restri
                 }
             }
             if (kt0 + kBN - 1 > q_base || kt0 + kBN - 1 >= S) {   // diagonal or tail: key > query / key >= S
+                keep_branch();
 #pragma unroll
                 for (int ks = 0; ks < 2; ++ks) {
                     const int l0 = q_lim0 - kt0 - 32 * ks, l1 = q_lim1 - kt0 - 32 * ks;
@@ -217,6 +227,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const T* __restri
                 // on the other queries of the wave.
                 const bool need = mx > m_i[cb] + 8.f;
                 if (wave_any(need)) {
+                    keep_branch();
                     const float m_new = need ? mx : m_i[cb];
                     const float alpha = need ? fast_exp2(m_i[cb] - m_new) : 1.f;
                     m_i[cb] = m_new;
@@ -307,7 +318,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_dq_kernel(const T* __restric
 
     int64_t bh; int qb;
     block_order(a, true, bh, qb);
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, wave = wave_id();
     const int col = lane & 31, h = lane >> 5;
     const int64_t S = a.S;
     const T* Qh = Q + bh * S * D;
@@ -344,14 +355,18 @@ __global__ __launch_bounds__(kThreads, 2) void attn_dq_kernel(const T* __restric
     const int q_lim0 = (int)((q_base + col < S - 1 ? q_base + col : S - 1) - 4 * h);
     const int q_lim1 = (int)((q_base + 32 + col < S - 1 ? q_base + 32 + col : S - 1) - 4 * h);
 
+    const uint32_t last_row = (uint32_t)(S - 1);
+    const uint32_t col_stride = (uint32_t)(a.S_pad * sizeof(T));
     auto stage = [&](int t, unsigned char* b) {
-        auto clamp = [&](int r) {
-            const int64_t row = (int64_t)t * kBN + r;
-            return row < S ? row : S - 1;
+        const uint32_t r0 = (uint32_t)t * kBN;
+        auto rows = [&](int r) {   // rows past S repeat row S - 1
+            const uint32_t row = r0 + r < last_row ? r0 + r : last_row;
+            return row * (uint32_t)RROWB;
         };
-        stage_tile<RROWB, RBYTES>(b, [&](int r) { return Kh + clamp(r) * D; });
-        stage_tile<RROWB, RBYTES>(b + RBYTES, [&](int r) { return Vh + clamp(r) * D; });
-        stage_tile<CROWB, CBYTES>(b + 2 * RBYTES, [&](int r) { return KTh + r * a.S_pad + (int64_t)t * kBN; });
+        stage_tile<RROWB, RBYTES, 4>(b, Kh, rows);
+        stage_tile<RROWB, RBYTES, 4>(b + RBYTES, Vh, rows);
+        stage_tile<CROWB, CBYTES, 4>(b + 2 * RBYTES, reinterpret_cast<const unsigned char*>(KTh) + (int64_t)t * CROWB,
+                                     [&](int r) { return (uint32_t)r * col_stride; });
     };
     stage(0, smem);
     wait_tiles_and_sync();
@@ -377,6 +392,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_dq_kernel(const T* __restric
                 mma_k16(dp[1], vf, df[1][c]);
             }
             if (kbase + 31 > q_base || kbase + 31 >= S) {   // diagonal or tail
+                keep_branch();
                 const int l0 = q_lim0 - (int)kbase, l1 = q_lim1 - (int)kbase;
 #pragma unroll
                 for (int j = 0; j < 16; ++j) {
@@ -447,7 +463,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_dkdv_kernel(const T* __r
 
     int64_t bh; int kb;
     block_order(a, false, bh, kb);
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, wave = wave_id();
     const int col = lane & 31, h = lane >> 5;
     const int64_t S = a.S;
     const T* Qh = Q + bh * S * D;
@@ -483,24 +499,26 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_dkdv_kernel(const T* __r
             dv[kc][db] = floatx16{};
         }
 
-    const int lane_w = threadIdx.x & 63, wave_w = threadIdx.x >> 6;
+    const uint32_t last_row = (uint32_t)(S - 1);
+    const uint32_t col_stride = (uint32_t)(a.S_pad * sizeof(T));
     auto stage = [&](int t, unsigned char* b) {
-        auto clamp = [&](int r) {
-            const int64_t row = (int64_t)t * kBN + r;
-            return row < S ? row : S - 1;
+        const uint32_t r0 = (uint32_t)t * kBN;
+        auto rows = [&](int r) {   // rows past S repeat row S - 1
+            const uint32_t row = r0 + r < last_row ? r0 + r : last_row;
+            return row * (uint32_t)RROWB;
         };
-        auto qrow = [&](int r) { return Qh + clamp(r) * D; };
-        auto dorow = [&](int r) { return dOh + clamp(r) * D; };
-        auto qtrow = [&](int r) { return QTh + r * a.S_pad + (int64_t)t * kBN; };
-        auto dotrow = [&](int r) { return dOTh + r * a.S_pad + (int64_t)t * kBN; };
-        stage_tile<RROWB, RBYTES, decltype(qrow), NW>(b, qrow);
-        stage_tile<RROWB, RBYTES, decltype(dorow), NW>(b + RBYTES, dorow);
-        stage_tile<CROWB, CBYTES, decltype(qtrow), NW>(b + 2 * RBYTES, qtrow);
-        stage_tile<CROWB, CBYTES, decltype(dotrow), NW>(b + 2 * RBYTES + CBYTES, dotrow);
+        auto cols = [&](int r) { return (uint32_t)r * col_stride; };
+        stage_tile<RROWB, RBYTES, NW>(b, Qh, rows);
+        stage_tile<RROWB, RBYTES, NW>(b + RBYTES, dOh, rows);
+        stage_tile<CROWB, CBYTES, NW>(b + 2 * RBYTES,
+                                      reinterpret_cast<const unsigned char*>(QTh) + (int64_t)t * CROWB, cols);
+        stage_tile<CROWB, CBYTES, NW>(b + 2 * RBYTES + CBYTES,
+                                      reinterpret_cast<const unsigned char*>(dOTh) + (int64_t)t * CROWB, cols);
         // the tile's 64 log-sum-exps (wave 0) and D values (wave 1), 4 bytes per lane
-        if (wave_w < 2) {
-            const float* src = (wave_w == 0 ? LSEh : Dh) + clamp(lane_w);
-            __builtin_amdgcn_global_load_lds(src, (lds_void*)(b + OFF_F + wave_w * kBN * 4), 4, 0, 0);
+        if (wave < 2) {
+            const int64_t row = (int64_t)t * kBN + lane;
+            const float* src = (wave == 0 ? LSEh : Dh) + (row < S ? row : S - 1);
+            __builtin_amdgcn_global_load_lds(src, (lds_void*)(b + OFF_F + wave * kBN * 4), 4, 0, 0);
         }
     };
 
@@ -539,6 +557,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_dkdv_kernel(const T* __r
                 }
             }
             if (k_base + 32 * KC - 1 > qt0 || qt0 + kBN - 1 >= S) {   // diagonal or tail
+                keep_branch();
 #pragma unroll
                 for (int qs = 0; qs < 2; ++qs)
 #pragma unroll

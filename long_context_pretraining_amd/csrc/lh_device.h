@@ -145,6 +145,14 @@ __device__ __forceinline__ float sum_halves(float x) {
 }
 __device__ __forceinline__ bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
 
+// Placed first in the body of a rarely taken uniform branch: an empty volatile
+// asm cannot be executed speculatively, so the compiler keeps the branch
+// instead of turning its body into selects that run on every pass.
+__device__ __forceinline__ void keep_branch() { asm volatile(""); }
+
+// Wave index as a uniform (scalar) value.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
 // Row offset (within a 32-row C tile) of register j, without the 4*(l/32) term.
 __device__ __forceinline__ constexpr int c_row0(int j) { return 8 * (j >> 2) + (j & 3); }
 
