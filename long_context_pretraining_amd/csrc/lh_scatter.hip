@@ -18,6 +18,10 @@ struct MapGeo {
     int p, L;
     int64_t off[LH_MAX_LEVELS + 1];
     int64_t pw[LH_MAX_LEVELS];
+    // n / p^l for 32-bit n as (umulhi(n, dmul) + n) >> dsh (round-up reciprocal,
+    // exact for n < 2^31), and 1 / p^l in f32
+    uint32_t dmul[LH_MAX_LEVELS], dsh[LH_MAX_LEVELS];
+    float inv[LH_MAX_LEVELS];
 };
 
 MapGeo make_geo(const LhGeom& g) {
@@ -25,8 +29,20 @@ MapGeo make_geo(const LhGeom& g) {
     m.BH = g.BH; m.N = g.N; m.d = g.d; m.S = g.S; m.S_pad = g.S_pad; m.Mu = g.Mu; m.M_total = g.M_total;
     m.p = g.p; m.L = g.L;
     for (int l = 0; l <= g.L; ++l) m.off[l] = g.off[l];
-    for (int l = 0; l < g.L; ++l) m.pw[l] = g.pw[l];
+    for (int l = 0; l < g.L; ++l) {
+        const uint64_t dv = (uint64_t)g.pw[l];
+        uint32_t sh = 0;
+        while ((1ull << sh) < dv) ++sh;
+        m.pw[l] = g.pw[l];
+        m.dsh[l] = sh;
+        m.dmul[l] = (uint32_t)((((uint64_t)1 << 32) * ((1ull << sh) - dv)) / dv + 1);
+        m.inv[l] = (float)(1.0 / (double)dv);
+    }
     return m;
+}
+
+__device__ __forceinline__ uint32_t div_pw(const MapGeo& G, int l, uint32_t n) {
+    return (__umulhi(n, G.dmul[l]) + n) >> G.dsh[l];
 }
 
 __device__ __forceinline__ int level_of(const MapGeo& G, int64_t flat) {
@@ -114,14 +130,25 @@ __global__ __launch_bounds__(kThreads) void scatter_fwd_kernel(const float* __re
         const int tl = task / nvec, vv = task - tl * nvec;
         const int64_t t = t0 + tl;
         if (t >= G.N) continue;
-        floatx8 acc = {};
-        for (int l = 0; l < G.L; ++l) {
-            const int64_t i = (t + 1) / G.pw[l] - 1;
-            if (i < 0) continue;
-            const int64_t g = gp[G.off[l] + i];
-            if (g < 0 || g >= G.S) continue;
-            acc += *reinterpret_cast<const floatx8*>(og + (bh * G.S + g) * G.d + vv * 8);
+        // all levels' slot lookups first, then all row loads: independent memory operations
+        int32_t gl[LH_MAX_LEVELS];
+#pragma unroll
+        for (int l = 0; l < LH_MAX_LEVELS; ++l) {
+            gl[l] = -1;
+            if (l < G.L) {
+                const uint32_t i1 = div_pw(G, l, (uint32_t)(t + 1));
+                if (i1 > 0) gl[l] = gp[G.off[l] + i1 - 1];
+            }
         }
+        floatx8 x[LH_MAX_LEVELS];
+#pragma unroll
+        for (int l = 0; l < LH_MAX_LEVELS; ++l) {
+            x[l] = floatx8{};
+            if (gl[l] >= 0 && gl[l] < G.S) x[l] = *reinterpret_cast<const floatx8*>(og + (bh * G.S + gl[l]) * G.d + vv * 8);
+        }
+        floatx8 acc = x[0];
+#pragma unroll
+        for (int l = 1; l < LH_MAX_LEVELS; ++l) acc += x[l];
         OV out;
 #pragma unroll
         for (int e = 0; e < 8; ++e) out[e] = static_cast<T>(acc[e]);
@@ -149,23 +176,57 @@ __global__ __launch_bounds__(kThreads) void scatter_bwd_kernel(const T* __restri
     const int nvec = (int)(G.d / VEC);
     T* tile = reinterpret_cast<T*>(smem);
     float* dpart = reinterpret_cast<float*>(smem + sizeof(T) * kRows * ld);
+    __shared__ int64_t s_lo[kRows];
+    __shared__ int s_len[kRows], s_order[kRows];
     const int64_t bh = blockIdx.y, s0 = (int64_t)blockIdx.x * kRows;
+    // Token range of each slot, then the slots ranked by range length (longest
+    // first, ties by slot), so the lanes of a wave sum ranges of similar length.
+    if (threadIdx.x < kRows) {
+        const int64_t s = s0 + threadIdx.x;
+        const int64_t flat = s < G.S ? gidx[bh * G.S + s] : -1;
+        int64_t lo = 0;
+        int len = 0;
+        if (flat >= 0 && flat < G.M_total) {
+            const int l = level_of(G, flat);
+            lo = (flat - G.off[l] + 1) * G.pw[l] - 1;
+            const int64_t hi = (lo + G.pw[l] - 1) < (G.N - 1) ? (lo + G.pw[l] - 1) : (G.N - 1);
+            len = (int)(hi - lo + 1);
+        }
+        s_lo[threadIdx.x] = lo;
+        s_len[threadIdx.x] = len;
+    }
+    __syncthreads();
+    if (threadIdx.x < kRows) {
+        const int me = threadIdx.x, len = s_len[me];
+        int rank = 0;
+        for (int j = 0; j < kRows; ++j) rank += (s_len[j] > len) || (s_len[j] == len && j < me);
+        s_order[rank] = me;
+    }
+    __syncthreads();
     for (int task = threadIdx.x; task < kRows * nvec; task += kThreads) {
-        const int sl = task / nvec, vv = task - sl * nvec;
+        const int rk = task / nvec, vv = task - rk * nvec;
+        const int sl = s_order[rk];
         const int64_t s = s0 + sl;
         VT r = {};
         float dp = 0.f;
-        const int64_t flat = s < G.S ? gidx[bh * G.S + s] : -1;
-        if (flat >= 0 && flat < G.M_total) {
-            const int l = level_of(G, flat);
-            const int64_t i = flat - G.off[l];
-            const int64_t lo = (i + 1) * G.pw[l] - 1;
-            const int64_t hi = (lo + G.pw[l] - 1) < (G.N - 1) ? (lo + G.pw[l] - 1) : (G.N - 1);
+        const int len = s_len[sl];
+        if (len > 0) {
+            const T* src = dout + (bh * G.N + s_lo[sl]) * G.d + vv * VEC;
             float acc[VEC];
 #pragma unroll
             for (int e = 0; e < VEC; ++e) acc[e] = 0.f;
-            for (int64_t t = lo; t <= hi; ++t) {
-                const VT x = *reinterpret_cast<const VT*>(dout + (bh * G.N + t) * G.d + vv * VEC);
+            int t = 0;
+            for (; t + 4 <= len; t += 4) {   // four independent loads per step, summed in token order
+                VT x[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) x[u] = *reinterpret_cast<const VT*>(src + (int64_t)(t + u) * G.d);
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+#pragma unroll
+                    for (int e = 0; e < VEC; ++e) acc[e] += to_f(x[u][e]);
+            }
+            for (; t < len; ++t) {
+                const VT x = *reinterpret_cast<const VT*>(src + (int64_t)t * G.d);
 #pragma unroll
                 for (int e = 0; e < VEC; ++e) acc[e] += to_f(x[e]);
             }
@@ -214,16 +275,24 @@ __global__ __launch_bounds__(kThreads) void gpool_bwd_kernel(const float* __rest
         const int tl = task / nvec, vv = task - tl * nvec;
         const int64_t t = t0 + tl;
         if (t >= G.N) continue;
+        // all levels' slot lookups first, then all row loads: independent memory operations
+        int32_t gl[LH_MAX_LEVELS];
+#pragma unroll
+        for (int l = 0; l < LH_MAX_LEVELS; ++l) gl[l] = l < G.L ? gp[G.off[l] + div_pw(G, l, (uint32_t)t)] : -1;
+        floatx8 x[LH_MAX_LEVELS];
+#pragma unroll
+        for (int l = 0; l < LH_MAX_LEVELS; ++l) {
+            x[l] = floatx8{};
+            if (gl[l] >= 0 && gl[l] < G.S) x[l] = *reinterpret_cast<const floatx8*>(dxg + (bh * G.S + gl[l]) * G.d + vv * 8);
+        }
         float acc[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[e] = 0.f;
-        for (int l = 0; l < G.L; ++l) {
-            const int64_t g = gp[G.off[l] + t / G.pw[l]];
-            if (g < 0 || g >= G.S) continue;
-            const floatx8 x = *reinterpret_cast<const floatx8*>(dxg + (bh * G.S + g) * G.d + vv * 8);
-            const float den = (float)G.pw[l];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) acc[e] += x[e] / den;
+        for (int l = 0; l < LH_MAX_LEVELS; ++l) {
+            const float w = l < G.L ? G.inv[l] : 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[e] = fmaf(x[l][e], w, acc[e]);
         }
         typename Frag<T>::type r;
 #pragma unroll
