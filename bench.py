@@ -41,7 +41,90 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="also run one plain device copy of 1 GiB (scales rocprofv3 byte counters)")
+    ap.add_argument("--pmc-summary", nargs="+", metavar="DIR",
+                    help="print per-dispatch counter averages from rocprofv3 --pmc output directories and exit")
     return ap.parse_args()
+
+
+# Files whose content determines the attention kernels' code: a stored HBM
+# traffic figure is reported only while they are unchanged.
+ATTN_SOURCES = ["long_context_pretraining_amd/csrc/lh_attention.hip", "long_context_pretraining_amd/csrc/lh_device.h",
+                "long_context_pretraining_amd/csrc/lh_internal.h"]
+TRAFFIC_PROFILE = "profiles/{kernel}_98k_k1536_hbm_traffic.md"
+
+
+def sources_sha256(paths):
+    import hashlib
+    h = hashlib.sha256()
+    root = os.path.dirname(os.path.abspath(__file__))
+    for p in paths:
+        with open(os.path.join(root, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def stored_traffic(kernel):
+    """HBM bytes per launch of `kernel` from its committed counter summary
+    (FETCH_SIZE + WRITE_SIZE, each scaled by a plain copy of known size), or
+    None when there is none or the kernel sources changed since."""
+    root = os.path.dirname(os.path.abspath(__file__))
+    path = os.path.join(root, TRAFFIC_PROFILE.format(kernel=kernel))
+    if not os.path.exists(path) or not kernel.startswith("attn"):
+        return None
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and line.startswith("- "):
+                key, val = line[2:].split(":", 1)
+                fields[key.strip()] = val.strip().strip("`")
+    if fields.get("sources_sha256") != sources_sha256(ATTN_SOURCES):
+        return None
+    return int(fields["hbm_bytes_per_launch"])
+
+
+def short_kernel_name(name):
+    import re
+    m = re.search(r"_GLOBAL__N_1(\d+)", name)   # mangled: <length><identifier>
+    if m:
+        return name[m.end():m.end() + int(m.group(1))]
+    m = re.search(r"(\w+)(?:<|\()", name)
+    return m.group(1) if m else name[:40]
+
+
+def pmc_summary(dirs):
+    """Markdown tables from rocprofv3 --output-format csv directories: the
+    kernel statistics of a --kernel-trace --stats run, and per-dispatch
+    counter averages per kernel of --pmc runs."""
+    import csv
+    import glob
+    for d in dirs:
+        for path in glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True):
+            print("| kernel | calls | total ms | avg us | min us | max us |")
+            print("|---|---:|---:|---:|---:|---:|")
+            with open(path) as f:
+                for r in csv.DictReader(f):
+                    print(f"| {short_kernel_name(r['Name'])} | {r['Calls']} | {int(r['TotalDurationNs']) / 1e6:.3f} | "
+                          f"{float(r['AverageNs']) / 1e3:.1f} | {int(r['MinNs']) / 1e3:.1f} | {int(r['MaxNs']) / 1e3:.1f} |")
+            print()
+    agg, cnt = {}, {}
+    for d in dirs:
+        for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            with open(path) as f:
+                for r in csv.DictReader(f):
+                    short = short_kernel_name(r["Kernel_Name"])
+                    key = (short, r["Counter_Name"])
+                    agg[key] = agg.get(key, 0.0) + float(r["Counter_Value"])
+                    cnt[key] = cnt.get(key, 0) + 1
+    if not agg:
+        return
+    counters = sorted({c for _, c in agg})
+    kernels = sorted({k for k, _ in agg})
+    print("| kernel | " + " | ".join(f"{c} (avg/dispatch)" for c in counters) + " | dispatches |")
+    print("|---|" + "---:|" * (len(counters) + 1))
+    for k in kernels:
+        vals = [f"{agg[(k, c)] / cnt[(k, c)]:.1f}" if (k, c) in agg else "" for c in counters]
+        n = max(cnt.get((k, c), 0) for c in counters)
+        print(f"| {k} | " + " | ".join(vals) + f" | {n} |")
 
 
 class HipEvents:
@@ -121,6 +204,9 @@ def cpu_baseline(w, q, k, v, dout, nheads=6):
 
 def main():
     args = parse()
+    if args.pmc_summary:
+        pmc_summary(args.pmc_summary)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py runs on exactly one GPU: the layer is measured per GPU and this build has no "
@@ -186,12 +272,12 @@ def main():
         peak = MFMA_BF16_PEAK_TFS if w.dtype == "bf16" else MFMA_F32_PEAK_TFS
         achieved = work / (dom_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
-                "frac": round(achieved / peak, 4), "traffic": None, "kernel": dominant,
+                "frac": round(achieved / peak, 4), "traffic": stored_traffic(dominant), "kernel": dominant,
                 "kernel_ms": round(dom_ms, 4), "work_per_launch": work}
     else:
         achieved = work / (dom_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None, "kernel": dominant,
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": stored_traffic(dominant), "kernel": dominant,
                 "kernel_ms": round(dom_ms, 4), "work_per_launch": work}
 
     # dense causal attention baseline on the same GPU and inputs
