@@ -102,14 +102,15 @@ typedef struct {
     size_t fwd_off[8];
     /* Inside the backward workspace:
      *   BWD_DO, BWD_DOT  dO~ [B,H,S,d] and transposed [B,H,d,S_pad] (same slot order), dtype
-     *   BWD_D            rowsum(dO~ * O~) [B,H,S] f32
+     *   BWD_NEG_D        -rowsum(dO~ * O~) [B,H,S] f32
      *   BWD_DQ, BWD_DK, BWD_DV  dQ~, dK~, dV~ [B,H,S,d] f32
-     *   BWD_LSE2         the row log-sum-exp in log2 units [B,H,S] f32 */
+     *   BWD_NEG_LSE      -(row log-sum-exp) / scale [B,H,S] f32: the offset of
+     *                    the unscaled scores q.k that P = exp(scale (q.k) - LSE) needs */
     size_t bwd_off[7];
 } lh_plan;
 
 enum { LH_FWD_QG = 0, LH_FWD_KG, LH_FWD_VG, LH_FWD_QT, LH_FWD_KT, LH_FWD_VT, LH_FWD_O, LH_FWD_LSE };
-enum { LH_BWD_DO = 0, LH_BWD_DOT, LH_BWD_D, LH_BWD_DQ, LH_BWD_DK, LH_BWD_DV, LH_BWD_LSE2 };
+enum { LH_BWD_DO = 0, LH_BWD_DOT, LH_BWD_NEG_D, LH_BWD_DQ, LH_BWD_DK, LH_BWD_DV, LH_BWD_NEG_LSE };
 
 /* Host only; validates the descriptor and fills `out`.  No device work. */
 lh_status lh_make_plan(const lh_desc* desc, lh_plan* out);

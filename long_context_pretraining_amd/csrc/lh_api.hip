@@ -209,12 +209,13 @@ lh_status lh_backward(const lh_desc* desc, const int32_t* gidx, const int32_t* g
     const float* lse = (const float*)at(fwd_ws, P.fwd_off[LH_FWD_LSE]);
     void* dog = at(bwd_ws, P.bwd_off[LH_BWD_DO]);
     void* dogT = at(bwd_ws, P.bwd_off[LH_BWD_DOT]);
-    float* Dv = (float*)at(bwd_ws, P.bwd_off[LH_BWD_D]);
-    float* lse2 = (float*)at(bwd_ws, P.bwd_off[LH_BWD_LSE2]);
+    float* nd = (float*)at(bwd_ws, P.bwd_off[LH_BWD_NEG_D]);
+    float* nl = (float*)at(bwd_ws, P.bwd_off[LH_BWD_NEG_LSE]);
     float* dxg[3] = {(float*)at(bwd_ws, P.bwd_off[LH_BWD_DQ]), (float*)at(bwd_ws, P.bwd_off[LH_BWD_DK]),
                      (float*)at(bwd_ws, P.bwd_off[LH_BWD_DV])};
     hipError_t e = probed(LH_KERNEL_SCATTER_BWD, st, [&] {
-        return launch_scatter_bwd(g, desc->dtype, dout, og, gidx, lse, dog, dogT, Dv, lse2, st);
+        return launch_scatter_bwd(g, desc->dtype, dout, og, gidx, lse, softmax_scale(desc), dog, dogT, nd, nl,
+                                  st);
     });
     const void* Qg = at(fwd_ws, P.fwd_off[LH_FWD_QG]);
     const void* Kg = at(fwd_ws, P.fwd_off[LH_FWD_KG]);
@@ -223,11 +224,11 @@ lh_status lh_backward(const lh_desc* desc, const int32_t* gidx, const int32_t* g
     if (e == hipSuccess)
         e = probed(LH_KERNEL_ATTN_DKDV, st, [&] {
             return launch_attn_dkdv(a, desc->dtype, true, Qg, Kg, Vg, at(fwd_ws, P.fwd_off[LH_FWD_QT]), dog, dogT,
-                                    lse2, Dv, dxg[1], dxg[2], st);
+                                    nl, nd, dxg[1], dxg[2], st);
         });
     if (e == hipSuccess)
         e = probed(LH_KERNEL_ATTN_DQ, st, [&] {
-            return launch_attn_dq(a, desc->dtype, true, Qg, Kg, Vg, at(fwd_ws, P.fwd_off[LH_FWD_KT]), dog, lse2, Dv,
+            return launch_attn_dq(a, desc->dtype, true, Qg, Kg, Vg, at(fwd_ws, P.fwd_off[LH_FWD_KT]), dog, nl, nd,
                                   dxg[0], st);
         });
     if (e == hipSuccess) {
@@ -276,24 +277,25 @@ lh_status dense_causal_attn_backward(const lh_desc* desc, const void* q, const v
     void* qT = ws;
     void* kT = at(ws, dT);
     void* doT = at(ws, 2 * dT);
-    float* Dv = (float*)at(ws, 3 * dT);
-    float* lse2 = (float*)at(ws, 3 * dT + align_up((size_t)BH * N * 4));
+    float* nd = (float*)at(ws, 3 * dT);
+    float* nl = (float*)at(ws, 3 * dT + align_up((size_t)BH * N * 4));
     const float* o32 = (const float*)at(fwd_ws, dT);
     hipError_t e = launch_transpose(desc->dtype, BH, N, N_pad, desc->d, q, qT, st);
     if (e == hipSuccess) e = launch_transpose(desc->dtype, BH, N, N_pad, desc->d, k, kT, st);
     if (e == hipSuccess)
         e = probed(LH_KERNEL_DENSE_PREP, st, [&] {
-            return launch_dense_bwd_prep(desc->dtype, BH, N, N_pad, desc->d, dout, o32, lse, doT, Dv, lse2, st);
+            return launch_dense_bwd_prep(desc->dtype, BH, N, N_pad, desc->d, dout, o32, lse, softmax_scale(desc),
+                                         doT, nd, nl, st);
         });
     AttnArgs a{BH, N, N_pad, desc->d, softmax_scale(desc)};
     const bool f32 = desc->dtype == LH_F32;
     if (e == hipSuccess)
         e = probed(LH_KERNEL_ATTN_DKDV, st, [&] {
-            return launch_attn_dkdv(a, desc->dtype, f32, q, k, v, qT, dout, doT, lse2, Dv, dk, dv, st);
+            return launch_attn_dkdv(a, desc->dtype, f32, q, k, v, qT, dout, doT, nl, nd, dk, dv, st);
         });
     if (e == hipSuccess)
         e = probed(LH_KERNEL_ATTN_DQ, st,
-                   [&] { return launch_attn_dq(a, desc->dtype, f32, q, k, v, kT, dout, lse2, Dv, dq, st); });
+                   [&] { return launch_attn_dq(a, desc->dtype, f32, q, k, v, kT, dout, nl, nd, dq, st); });
     return dev(e);
 }
 

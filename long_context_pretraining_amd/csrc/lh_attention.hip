@@ -30,8 +30,7 @@ constexpr int kWaveRows = 64;   // queries (fwd, dQ) or keys (dK/dV) per wave
 constexpr int kBlockRows = 4 * kWaveRows;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr int kDkdvKC = 1;      // 32-key column blocks per dK/dV wave
-constexpr int kDkdvNW = 8;      // waves per dK/dV block (blocks of 32 * KC * NW keys)
+constexpr int kDkdvNW = 8;      // waves per dK/dV block (32 keys each; d = 128: 4)
 
 struct AttnK {
     int64_t BH, S, S_pad;
@@ -57,6 +56,8 @@ typedef __attribute__((address_space(3))) void lds_void;
 
 template <int ROWB>
 __device__ __forceinline__ int swz_key(int row) {
+    static_assert(ROWB == 64 || ROWB == 128 || ROWB == 256, "row tiles of 64, 128 or 256 bytes");
+    if (ROWB == 64) return ((row >> 1) ^ (row >> 3)) & 3;
     return ROWB == 128 ? ((row ^ (row >> 3)) & 7) : (row & 15);
 }
 template <int ROWB>
@@ -87,6 +88,10 @@ __device__ __forceinline__ void stage_tile(unsigned char* tile, const void* base
 template <typename T, int ROWB>
 __device__ __forceinline__ typename Frag<T>::type tile_frag(const unsigned char* tile, int row, int e0);
 template <>
+__device__ __forceinline__ bf16x8 tile_frag<bf16, 64>(const unsigned char* tile, int row, int e0) {
+    return *reinterpret_cast<const bf16x8*>(tile + swz<64>(row, e0 >> 3));
+}
+template <>
 __device__ __forceinline__ bf16x8 tile_frag<bf16, 128>(const unsigned char* tile, int row, int e0) {
     return *reinterpret_cast<const bf16x8*>(tile + swz<128>(row, e0 >> 3));
 }
@@ -94,14 +99,22 @@ template <>
 __device__ __forceinline__ bf16x8 tile_frag<bf16, 256>(const unsigned char* tile, int row, int e0) {
     return *reinterpret_cast<const bf16x8*>(tile + swz<256>(row, e0 >> 3));
 }
-template <>
-__device__ __forceinline__ floatx8 tile_frag<float, 256>(const unsigned char* tile, int row, int e0) {
-    const floatx4 a = *reinterpret_cast<const floatx4*>(tile + swz<256>(row, e0 >> 2));
-    const floatx4 b = *reinterpret_cast<const floatx4*>(tile + swz<256>(row, (e0 >> 2) + 1));
+template <int ROWB>
+__device__ __forceinline__ floatx8 tile_frag_f32(const unsigned char* tile, int row, int e0) {
+    const floatx4 a = *reinterpret_cast<const floatx4*>(tile + swz<ROWB>(row, e0 >> 2));
+    const floatx4 b = *reinterpret_cast<const floatx4*>(tile + swz<ROWB>(row, (e0 >> 2) + 1));
     floatx8 r;
     r.lo = a;
     r.hi = b;
     return r;
+}
+template <>
+__device__ __forceinline__ floatx8 tile_frag<float, 128>(const unsigned char* tile, int row, int e0) {
+    return tile_frag_f32<128>(tile, row, e0);
+}
+template <>
+__device__ __forceinline__ floatx8 tile_frag<float, 256>(const unsigned char* tile, int row, int e0) {
+    return tile_frag_f32<256>(tile, row, e0);
 }
 
 __device__ __forceinline__ void wait_tiles_and_sync() {
@@ -308,8 +321,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const T* __restri
 template <typename T, int D, typename OutT>
 __global__ __launch_bounds__(kThreads, 2) void attn_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K,
                                                            const T* __restrict__ V, const T* __restrict__ KT,
-                                                           const T* __restrict__ dO, const float* __restrict__ LSE,
-                                                           const float* __restrict__ Dv, OutT* __restrict__ dQ,
+                                                           const T* __restrict__ dO, const float* __restrict__ NL,
+                                                           const float* __restrict__ ND, OutT* __restrict__ dQ,
                                                            AttnK a) {
     typedef typename Frag<T>::type F;
     constexpr int RROWB = D * (int)sizeof(T), CROWB = kBN * (int)sizeof(T);
@@ -334,7 +347,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_dq_kernel(const T* __restric
     const int ntiles = (int)(q_last_blk / kBN) + 1;
 
     F qf[2][D / 16], df[2][D / 16];
-    float lse2[2], dd[2];
+    float nlc[2], nd[2];   // -LSE in log2 units, -D
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb) {
         const int64_t q = q_base + 32 * cb + col;
@@ -344,8 +357,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_dq_kernel(const T* __restric
             qf[cb][c] = load8_or_zero(Qh + q * D + 16 * c + 8 * h, ok);
             df[cb][c] = load8_or_zero(dOh + q * D + 16 * c + 8 * h, ok);
         }
-        lse2[cb] = ok ? LSE[bh * S + q] : 0.f;   // log2 units
-        dd[cb] = ok ? Dv[bh * S + q] : 0.f;
+        nlc[cb] = ok ? NL[bh * S + q] * a.scale_log2 : 0.f;
+        nd[cb] = ok ? ND[bh * S + q] : 0.f;
     }
     floatx16 acc[2][D / 32];
 #pragma unroll
@@ -404,8 +417,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_dq_kernel(const T* __restric
             for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
                 for (int j = 0; j < 16; ++j) {
-                    const float pv = fast_exp2(fmaf(s[cb][j], a.scale_log2, -lse2[cb]));
-                    s[cb][j] = pv * (dp[cb][j] - dd[cb]);
+                    const float pv = fast_exp2(fmaf(s[cb][j], a.scale_log2, nlc[cb]));
+                    s[cb][j] = pv * (dp[cb][j] + nd[cb]);
                 }
 #pragma unroll
             for (int c2 = 0; c2 < 2; ++c2) {
@@ -443,22 +456,44 @@ __global__ __launch_bounds__(kThreads, 2) void attn_dq_kernel(const T* __restric
 }
 
 // ---------------------------------------------------------------------------
-// dK, dV: per 256-key block, over query tiles from the diagonal on:
-// S = Q K^T, P = exp(S - LSE), dP = dO V^T, dS = P (dP - D),
+// dK, dV: per block of 32*NW keys (each wave owns 32 key columns), over the
+// queries from the diagonal on, in steps of 32 queries:
+// S = Q K^T - LSE/scale, P = exp(scale S), dP' = dO V^T - D, dS = P dP',
 // dV^T += dO^T P, dK^T += Q^T dS  (P and dS as bf16 hi + lo parts).
+// The -LSE/scale and -D terms enter as the initial accumulators of the two
+// products, so they cost no vector instruction.
+//
+// Software pipeline: while a wave turns step u's scores into P and dS and
+// accumulates dV and dK (vector work plus 16 matrix products), it already
+// computes step u+1's two score products (8 independent matrix products), so
+// the matrix cores and the vector units have independent work side by side.
+// LDS: query tiles of TQ rows.  Row tiles (Q, dO, -LSE/scale, -D) are needed
+// one step ahead and live in three buffers; column tiles (Q^T, dO^T) in two.
+// Tile t + 2's rows and tile t + 1's columns are loaded while tile t is used;
+// one barrier per tile.
 // ---------------------------------------------------------------------------
-template <typename T, int D, typename OutT, int KC, int NW>
-__global__ __launch_bounds__(64 * NW, 8 / NW) void attn_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K,
-                                                             const T* __restrict__ V, const T* __restrict__ QT,
-                                                             const T* __restrict__ dO, const T* __restrict__ dOT,
-                                                             const float* __restrict__ LSE,
-                                                             const float* __restrict__ Dv, OutT* __restrict__ dK,
-                                                             OutT* __restrict__ dV, AttnK a) {
+template <typename T, int D, int TQ>
+struct DkdvLds {
+    static constexpr int RROWB = D * (int)sizeof(T);   // bytes per row of a row tile
+    static constexpr int CROWB = TQ * (int)sizeof(T);  // bytes per row of a column tile
+    static constexpr int RT = TQ * RROWB;              // one row tile
+    static constexpr int CT = D * CROWB;               // one column tile
+    static constexpr int RBUF = 2 * RT + 2 * 256;      // Q, dO, -LSE/scale, -D
+    static constexpr int CBUF = 2 * CT;                // Q^T, dO^T
+    static constexpr int BYTES = 3 * RBUF + 2 * CBUF;
+};
+
+template <typename T, int D, typename OutT, int NW, int TQ>
+__global__ __launch_bounds__(64 * NW, 1) void attn_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K,
+                                                               const T* __restrict__ V, const T* __restrict__ QT,
+                                                               const T* __restrict__ dO, const T* __restrict__ dOT,
+                                                               const float* __restrict__ NL,
+                                                               const float* __restrict__ ND, OutT* __restrict__ dK,
+                                                               OutT* __restrict__ dV, AttnK a) {
     typedef typename Frag<T>::type F;
-    constexpr int RROWB = D * (int)sizeof(T), CROWB = kBN * (int)sizeof(T);
-    constexpr int RBYTES = kBN * RROWB, CBYTES = D * CROWB;
-    constexpr int OFF_F = 2 * RBYTES + 2 * CBYTES, BUF = OFF_F + 2 * kBN * 4;
-    constexpr int BK = 32 * KC * NW;           // keys per block: NW waves of 32*KC keys
+    typedef DkdvLds<T, D, TQ> L;
+    constexpr int NSTEP = TQ / 32;
+    constexpr int RROWB = L::RROWB, CROWB = L::CROWB;
     extern __shared__ __align__(16) unsigned char smem[];
 
     int64_t bh; int kb;
@@ -472,152 +507,174 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_dkdv_kernel(const T* __r
     const T* QTh = QT + bh * D * a.S_pad;
     const T* dOh = dO + bh * S * D;
     const T* dOTh = dOT + bh * D * a.S_pad;
-    const float* LSEh = LSE + bh * S;
-    const float* Dh = Dv + bh * S;
+    const float* NLh = NL + bh * S;
+    const float* NDh = ND + bh * S;
 
-    const int64_t k_blk0 = (int64_t)kb * BK;
-    const int64_t k_base = k_blk0 + wave * 32 * KC;
-    const int t0 = (int)(k_blk0 / kBN);
-    const int ntiles_total = (int)((S + kBN - 1) / kBN);
+    const int64_t k_blk0 = (int64_t)kb * (32 * NW);
+    const int64_t k_base = k_blk0 + 32 * wave;
+    const int t0 = (int)(k_blk0 / TQ);
+    const int ntiles = (int)((S + TQ - 1) / TQ);
+    const int u_first = (int)(k_base / 32);       // the diagonal step (queries k_base .. k_base + 31)
 
-    F kf[KC][D / 16], vf[KC][D / 16];
-#pragma unroll
-    for (int kc = 0; kc < KC; ++kc) {
-        const int64_t key = k_base + 32 * kc + col;
+    F kf[D / 16], vf[D / 16];
+    {
+        const int64_t key = k_base + col;
 #pragma unroll
         for (int c = 0; c < D / 16; ++c) {
-            kf[kc][c] = load8_or_zero(Kh + key * D + 16 * c + 8 * h, key < S);
-            vf[kc][c] = load8_or_zero(Vh + key * D + 16 * c + 8 * h, key < S);
+            kf[c] = load8_or_zero(Kh + key * D + 16 * c + 8 * h, key < S);
+            vf[c] = load8_or_zero(Vh + key * D + 16 * c + 8 * h, key < S);
         }
     }
-    floatx16 dk[KC][D / 32], dv[KC][D / 32];
+    floatx16 dk[D / 32], dv[D / 32];
 #pragma unroll
-    for (int kc = 0; kc < KC; ++kc)
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-            dk[kc][db] = floatx16{};
-            dv[kc][db] = floatx16{};
-        }
+    for (int db = 0; db < D / 32; ++db) {
+        dk[db] = floatx16{};
+        dv[db] = floatx16{};
+    }
 
     const uint32_t last_row = (uint32_t)(S - 1);
     const uint32_t col_stride = (uint32_t)(a.S_pad * sizeof(T));
-    auto stage = [&](int t, unsigned char* b) {
-        const uint32_t r0 = (uint32_t)t * kBN;
+    auto rbuf = [&](int t) { return smem + (t % 3) * L::RBUF; };
+    auto cbuf = [&](int t) { return smem + 3 * L::RBUF + (t & 1) * L::CBUF; };
+    auto stage_rows = [&](int t) {
+        unsigned char* b = rbuf(t);
+        const uint32_t r0 = (uint32_t)t * TQ;
         auto rows = [&](int r) {   // rows past S repeat row S - 1
             const uint32_t row = r0 + r < last_row ? r0 + r : last_row;
             return row * (uint32_t)RROWB;
         };
-        auto cols = [&](int r) { return (uint32_t)r * col_stride; };
-        stage_tile<RROWB, RBYTES, NW>(b, Qh, rows);
-        stage_tile<RROWB, RBYTES, NW>(b + RBYTES, dOh, rows);
-        stage_tile<CROWB, CBYTES, NW>(b + 2 * RBYTES,
-                                      reinterpret_cast<const unsigned char*>(QTh) + (int64_t)t * CROWB, cols);
-        stage_tile<CROWB, CBYTES, NW>(b + 2 * RBYTES + CBYTES,
-                                      reinterpret_cast<const unsigned char*>(dOTh) + (int64_t)t * CROWB, cols);
-        // the tile's 64 log-sum-exps (wave 0) and D values (wave 1), 4 bytes per lane
+        stage_tile<RROWB, L::RT, NW>(b, Qh, rows);
+        stage_tile<RROWB, L::RT, NW>(b + L::RT, dOh, rows);
+        // 64 values of -LSE/scale (wave 0) and -D (wave 1), 4 bytes per lane
         if (wave < 2) {
-            const int64_t row = (int64_t)t * kBN + lane;
-            const float* src = (wave == 0 ? LSEh : Dh) + (row < S ? row : S - 1);
-            __builtin_amdgcn_global_load_lds(src, (lds_void*)(b + OFF_F + wave * kBN * 4), 4, 0, 0);
+            const uint32_t row = r0 + lane < last_row ? r0 + lane : last_row;
+            __builtin_amdgcn_global_load_lds((wave == 0 ? NLh : NDh) + row, (lds_void*)(b + 2 * L::RT + wave * 256),
+                                             4, 0, 0);
         }
     };
+    auto stage_cols = [&](int t) {
+        unsigned char* b = cbuf(t);
+        auto cols = [&](int r) { return (uint32_t)r * col_stride; };
+        stage_tile<CROWB, L::CT, NW>(b, reinterpret_cast<const unsigned char*>(QTh) + (int64_t)t * CROWB, cols);
+        stage_tile<CROWB, L::CT, NW>(b + L::CT, reinterpret_cast<const unsigned char*>(dOTh) + (int64_t)t * CROWB,
+                                     cols);
+    };
 
-    if (t0 < ntiles_total) stage(t0, smem);
-    wait_tiles_and_sync();
-
-    for (int t = t0; t < ntiles_total; ++t) {
-        const int buf = (t - t0) & 1;
-        if (t + 1 < ntiles_total) stage(t + 1, smem + (buf ^ 1) * BUF);
-        const unsigned char* lq = smem + buf * BUF;
-        const unsigned char* ldo = lq + RBYTES;
-        const unsigned char* lqt = lq + 2 * RBYTES;
-        const unsigned char* ldot = lqt + CBYTES;
-        const float* lf = reinterpret_cast<const float*>(lq + OFF_F);
-        const int64_t qt0 = (int64_t)t * kBN;
-        if (k_base <= qt0 + kBN - 1 && k_base < S) {   // some key of this wave precedes some query of the tile
-            // S = Q K^T and dP = dO V^T for both 32-query halves first
-            floatx16 sp[2][KC], dp[2][KC];
+    // Score products of one step: S' = Q K^T - LSE/scale and dP' = dO V^T - D
+    // for the 32 queries at row r0 of row tile rb.
+    auto scores = [&](const unsigned char* rb, int r0, floatx16& sp, floatx16& dp) {
+        const float* nl = reinterpret_cast<const float*>(rb + 2 * L::RT);
+        const float* nd = nl + 64;
 #pragma unroll
-            for (int qs = 0; qs < 2; ++qs) {
-                F qa[D / 16], da[D / 16];
+        for (int m = 0; m < 4; ++m) {
+            const floatx4 l4 = *reinterpret_cast<const floatx4*>(nl + r0 + 8 * m + 4 * h);
+            const floatx4 d4 = *reinterpret_cast<const floatx4*>(nd + r0 + 8 * m + 4 * h);
 #pragma unroll
-                for (int cc = 0; cc < D / 16; ++cc) {
-                    qa[cc] = tile_frag<T, RROWB>(lq, 32 * qs + col, 16 * cc + 8 * h);
-                    da[cc] = tile_frag<T, RROWB>(ldo, 32 * qs + col, 16 * cc + 8 * h);
-                }
-#pragma unroll
-                for (int kc = 0; kc < KC; ++kc) {
-                    sp[qs][kc] = floatx16{};
-                    dp[qs][kc] = floatx16{};
-#pragma unroll
-                    for (int cc = 0; cc < D / 16; ++cc) {
-                        mma_k16(sp[qs][kc], qa[cc], kf[kc][cc]);
-                        mma_k16(dp[qs][kc], da[cc], vf[kc][cc]);
-                    }
-                }
+            for (int i = 0; i < 4; ++i) {
+                sp[4 * m + i] = l4[i];
+                dp[4 * m + i] = d4[i];
             }
-            if (k_base + 32 * KC - 1 > qt0 || qt0 + kBN - 1 >= S) {   // diagonal or tail
-                keep_branch();
+        }
 #pragma unroll
-                for (int qs = 0; qs < 2; ++qs)
+        for (int cc = 0; cc < D / 16; ++cc) {
+            const F qa = tile_frag<T, RROWB>(rb, r0 + col, 16 * cc + 8 * h);
+            const F da = tile_frag<T, RROWB>(rb + L::RT, r0 + col, 16 * cc + 8 * h);
+            mma_k16(sp, qa, kf[cc]);
+            mma_k16(dp, da, vf[cc]);
+        }
+    };
+    // P, dS and the dV / dK products of one step (columns c0 .. c0+31 of column tile cb).
+    auto grads = [&](const unsigned char* cb, int c0, floatx16& sp, floatx16& dp) {
+        const float c = a.scale_log2;
 #pragma unroll
-                    for (int kc = 0; kc < KC; ++kc) {
-                        // row j (query qt0 + 32qs + 4h + c_row0(j)) is masked when the key is after it or it is past S
-                        const int kl = (int)(k_base + 32 * kc + col - qt0) - 32 * qs - 4 * h;
-                        const int sl = (int)(S - qt0) - 32 * qs - 4 * h;
+        for (int c2 = 0; c2 < 2; ++c2) {
 #pragma unroll
-                        for (int j = 0; j < 16; ++j)
-                            if (c_row0(j) < kl || c_row0(j) >= sl) sp[qs][kc][j] = -INFINITY;
-                    }
+            for (int e = 0; e < 8; ++e) {
+                const float pv = fast_exp2(sp[8 * c2 + e] * c);
+                sp[8 * c2 + e] = pv;
+                dp[8 * c2 + e] = pv * dp[8 * c2 + e];
             }
+            F ph, pl, gh, gl;
+            split_frag<T>(sp, c2, ph, pl);
+            split_frag<T>(dp, c2, gh, gl);
 #pragma unroll
-            for (int qs = 0; qs < 2; ++qs) {
-                float lrow[16], drow[16];
-#pragma unroll
-                for (int m = 0; m < 4; ++m) {
-                    const floatx4 l4 = *reinterpret_cast<const floatx4*>(lf + 32 * qs + 8 * m + 4 * h);
-                    const floatx4 d4 = *reinterpret_cast<const floatx4*>(lf + kBN + 32 * qs + 8 * m + 4 * h);
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        lrow[4 * m + i] = l4[i];   // log2 units
-                        drow[4 * m + i] = d4[i];
-                    }
-                }
-#pragma unroll
-                for (int kc = 0; kc < KC; ++kc) {
-#pragma unroll
-                    for (int j = 0; j < 16; ++j) {
-                        const float pv = fast_exp2(fmaf(sp[qs][kc][j], a.scale_log2, -lrow[j]));
-                        sp[qs][kc][j] = pv;
-                        dp[qs][kc][j] = pv * (dp[qs][kc][j] - drow[j]);
-                    }
-#pragma unroll
-                    for (int c2 = 0; c2 < 2; ++c2) {
-                        F ph, pl, gh, gl;
-                        split_frag<T>(sp[qs][kc], c2, ph, pl);
-                        split_frag<T>(dp[qs][kc], c2, gh, gl);
-#pragma unroll
-                        for (int db = 0; db < D / 32; ++db) {
-                            const F dof = tile_frag<T, CROWB>(ldot, 32 * db + col, 32 * qs + 16 * c2 + 8 * h);
-                            const F qtf = tile_frag<T, CROWB>(lqt, 32 * db + col, 32 * qs + 16 * c2 + 8 * h);
-                            mma_k16(dv[kc][db], dof, ph);
-                            mma_k16(dk[kc][db], qtf, gh);
-                            if (kSplitP<T>) {
-                                mma_k16(dv[kc][db], dof, pl);
-                                mma_k16(dk[kc][db], qtf, gl);
-                            }
-                        }
-                    }
+            for (int db = 0; db < D / 32; ++db) {
+                const F dof = tile_frag<T, CROWB>(cb + L::CT, 32 * db + col, c0 + 16 * c2 + 8 * h);
+                const F qtf = tile_frag<T, CROWB>(cb, 32 * db + col, c0 + 16 * c2 + 8 * h);
+                mma_k16(dv[db], dof, ph);
+                mma_k16(dk[db], qtf, gh);
+                if (kSplitP<T>) {
+                    mma_k16(dv[db], dof, pl);
+                    mma_k16(dk[db], qtf, gl);
                 }
             }
         }
-        wait_tiles_and_sync();
+    };
+    // Step v's mask: key after query (steps up to the diagonal) or query >= S.
+    auto needs_mask = [&](int v) { return v <= u_first || 32 * (int64_t)v + 31 >= S; };
+    auto mask = [&](floatx16& sp, int v) {
+        const int kl = (int)(k_base - 32 * (int64_t)v) + col - 4 * h;   // rows below kl precede the key
+        const int64_t sl64 = S - 32 * (int64_t)v - 4 * h;                 // rows from sl on are past S
+        const int sl = (int)(sl64 < 64 ? sl64 : 64);
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+            if (c_row0(j) < kl || c_row0(j) >= sl) sp[j] = -INFINITY;
+    };
+
+    // prologue: rows of the first two tiles, columns of the first
+    if (t0 < ntiles) {
+        stage_rows(t0);
+        stage_cols(t0);
+    }
+    if (t0 + 1 < ntiles) stage_rows(t0 + 1);
+    wait_tiles_and_sync();
+
+    // Every wave runs every step of the block from the first tile on: steps
+    // before its diagonal are fully masked (they add zeros), which keeps one
+    // uniform instruction stream per step.  Step u's products live in sp[u & 1].
+    floatx16 sp[2], dp[2];
+    const int u0 = t0 * NSTEP;
+    if (t0 < ntiles) {
+        scores(rbuf(t0), 0, sp[0], dp[0]);
+        mask(sp[0], u0);
+    }
+    // one step: the next step's score products, this step's gradients, then
+    // (rarely) the next step's mask
+    auto step = [&](int t, int qs, floatx16& sp_c, floatx16& dp_c, floatx16& sp_n, floatx16& dp_n) {
+        const int u = t * NSTEP + qs;
+        const bool last_in_tile = qs + 1 == NSTEP;
+        scores(last_in_tile ? rbuf(t + 1) : rbuf(t), last_in_tile ? 0 : 32 * (qs + 1), sp_n, dp_n);
+        grads(cbuf(t), 32 * qs, sp_c, dp_c);
+        if (needs_mask(u + 1)) {
+            keep_branch();
+            mask(sp_n, u + 1);
+        }
+    };
+    if constexpr (NSTEP == 2) {
+        for (int t = t0; t < ntiles; ++t) {
+            if (t + 2 < ntiles) stage_rows(t + 2);
+            if (t + 1 < ntiles) stage_cols(t + 1);
+            step(t, 0, sp[0], dp[0], sp[1], dp[1]);
+            step(t, 1, sp[1], dp[1], sp[0], dp[0]);
+            wait_tiles_and_sync();
+        }
+    } else {
+        for (int t = t0; t < ntiles; t += 2) {
+            if (t + 2 < ntiles) stage_rows(t + 2);
+            if (t + 1 < ntiles) stage_cols(t + 1);
+            step(t, 0, sp[0], dp[0], sp[1], dp[1]);
+            wait_tiles_and_sync();
+            if (t + 1 < ntiles) {
+                if (t + 3 < ntiles) stage_rows(t + 3);
+                if (t + 2 < ntiles) stage_cols(t + 2);
+                step(t + 1, 0, sp[1], dp[1], sp[0], dp[0]);
+                wait_tiles_and_sync();
+            }
+        }
     }
 
-#pragma unroll
-    for (int kc = 0; kc < KC; ++kc) {
-        const int64_t key = k_base + 32 * kc + col;
-        if (key >= S) continue;
+    const int64_t key = k_base + col;
+    if (key < S) {
         OutT* rk = dK + (bh * S + key) * D;
         OutT* rv = dV + (bh * S + key) * D;
 #pragma unroll
@@ -626,8 +683,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_dkdv_kernel(const T* __r
             for (int m = 0; m < 4; ++m)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    rk[32 * db + 8 * m + 4 * h + i] = static_cast<OutT>(dk[kc][db][4 * m + i] * a.scale);
-                    rv[32 * db + 8 * m + 4 * h + i] = static_cast<OutT>(dv[kc][db][4 * m + i]);
+                    rk[32 * db + 8 * m + 4 * h + i] = static_cast<OutT>(dk[db][4 * m + i] * a.scale);
+                    rv[32 * db + 8 * m + 4 * h + i] = static_cast<OutT>(dv[db][4 * m + i]);
                 }
     }
 }
@@ -636,8 +693,6 @@ template <typename T, int D>
 size_t fwd_lds() { return 2 * 2 * kBN * D * sizeof(T); }
 template <typename T, int D>
 size_t dq_lds() { return 2 * 3 * kBN * D * sizeof(T); }
-template <typename T, int D>
-size_t dkdv_lds() { return 2 * (4 * kBN * D * sizeof(T) + 2 * kBN * sizeof(float)); }
 
 AttnK make_k(const AttnArgs& a) {
     AttnK k{};
@@ -661,31 +716,36 @@ hipError_t fwd_t(const AttnArgs& a, const void* Q, const void* K, const void* VT
 
 template <typename T, int D, typename OutT>
 hipError_t dkdv_t(const AttnArgs& a, const void* Q, const void* K, const void* V, const void* QT, const void* dO,
-                  const void* dOT, const float* lse, const float* Dv, void* dK, void* dV, hipStream_t st) {
-    const AttnK k = make_k(a);
-    const size_t sh = dkdv_lds<T, D>();
-    constexpr int BK = 32 * kDkdvKC * kDkdvNW;
-    AttnK kk = k;
-    kk.nblk = (int)((a.S + BK - 1) / BK);
-    static const hipError_t attr = hipFuncSetAttribute((const void*)attn_dkdv_kernel<T, D, OutT, kDkdvKC, kDkdvNW>,
-                                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)sh);
+                  const void* dOT, const float* nl, const float* nd, void* dK, void* dV, hipStream_t st) {
+    // 64-query tiles where three row and two column buffers fit the LDS twice over, else 32
+    constexpr int TQ = (D * sizeof(T) <= 128) ? 64 : 32;
+    typedef DkdvLds<T, D, TQ> L;
+    static_assert(L::BYTES <= 160 * 1024, "dK/dV LDS budget");
+    // d = 128 keeps twice the key and accumulator registers: one wave per SIMD
+    constexpr int NW = D == 128 ? 4 : kDkdvNW;
+    AttnK k = make_k(a);
+    constexpr int BK = 32 * NW;
+    k.nblk = (int)((a.S + BK - 1) / BK);
+    auto kern = attn_dkdv_kernel<T, D, OutT, NW, TQ>;
+    static const hipError_t attr =
+        hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, L::BYTES);
     (void)attr;
-    attn_dkdv_kernel<T, D, OutT, kDkdvKC, kDkdvNW><<<dim3((unsigned)(kk.nblk * a.BH)), 64 * kDkdvNW, sh, st>>>(
-        (const T*)Q, (const T*)K, (const T*)V, (const T*)QT, (const T*)dO, (const T*)dOT, lse, Dv, (OutT*)dK,
-        (OutT*)dV, kk);
+    kern<<<dim3((unsigned)(k.nblk * a.BH)), 64 * NW, L::BYTES, st>>>((const T*)Q, (const T*)K, (const T*)V,
+                                                                         (const T*)QT, (const T*)dO, (const T*)dOT,
+                                                                         nl, nd, (OutT*)dK, (OutT*)dV, k);
     return hipGetLastError();
 }
 
 template <typename T, int D, typename OutT>
 hipError_t dq_t(const AttnArgs& a, const void* Q, const void* K, const void* V, const void* KT, const void* dO,
-                const float* lse, const float* Dv, void* dQ, hipStream_t st) {
+                const float* nl, const float* nd, void* dQ, hipStream_t st) {
     const AttnK k = make_k(a);
     const size_t sh = dq_lds<T, D>();
     static const hipError_t attr = hipFuncSetAttribute((const void*)attn_dq_kernel<T, D, OutT>,
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)sh);
     (void)attr;
     attn_dq_kernel<T, D, OutT><<<dim3((unsigned)(k.nblk * a.BH)), kThreads, sh, st>>>(
-        (const T*)Q, (const T*)K, (const T*)V, (const T*)KT, (const T*)dO, lse, Dv, (OutT*)dQ, k);
+        (const T*)Q, (const T*)K, (const T*)V, (const T*)KT, (const T*)dO, nl, nd, (OutT*)dQ, k);
     return hipGetLastError();
 }
 
@@ -699,9 +759,9 @@ hipError_t launch_attn_fwd(const AttnArgs& a, int dtype, const void* Q, const vo
 }
 
 hipError_t launch_attn_dkdv(const AttnArgs& a, int dtype, bool out_f32, const void* Q, const void* K, const void* V,
-                            const void* QT, const void* dO, const void* dOT, const float* lse, const float* Dv,
+                            const void* QT, const void* dO, const void* dOT, const float* nl, const float* nd,
                             void* dK, void* dV, hipStream_t st) {
-#define LH_DKDV(T, D, O) dkdv_t<T, D, O>(a, Q, K, V, QT, dO, dOT, lse, Dv, dK, dV, st)
+#define LH_DKDV(T, D, O) dkdv_t<T, D, O>(a, Q, K, V, QT, dO, dOT, nl, nd, dK, dV, st)
     if (dtype == LH_BF16) {
         if (a.d == 64) return out_f32 ? LH_DKDV(bf16, 64, float) : LH_DKDV(bf16, 64, bf16);
         return out_f32 ? LH_DKDV(bf16, 128, float) : LH_DKDV(bf16, 128, bf16);
@@ -711,9 +771,9 @@ hipError_t launch_attn_dkdv(const AttnArgs& a, int dtype, bool out_f32, const vo
 }
 
 hipError_t launch_attn_dq(const AttnArgs& a, int dtype, bool out_f32, const void* Q, const void* K, const void* V,
-                          const void* KT, const void* dO, const float* lse, const float* Dv, void* dQ,
+                          const void* KT, const void* dO, const float* nl, const float* nd, void* dQ,
                           hipStream_t st) {
-#define LH_DQ(T, D, O) dq_t<T, D, O>(a, Q, K, V, KT, dO, lse, Dv, dQ, st)
+#define LH_DQ(T, D, O) dq_t<T, D, O>(a, Q, K, V, KT, dO, nl, nd, dQ, st)
     if (dtype == LH_BF16) {
         if (a.d == 64) return out_f32 ? LH_DQ(bf16, 64, float) : LH_DQ(bf16, 64, bf16);
         return out_f32 ? LH_DQ(bf16, 128, float) : LH_DQ(bf16, 128, bf16);

@@ -33,17 +33,18 @@ hipError_t launch_gather(const LhGeom& g, int dtype, const void* q, const void* 
 // og: the sub-sequence output, kept in f32 [BH,S,d]
 hipError_t launch_scatter_fwd(const LhGeom& g, int dtype, const float* og, const int32_t* gpos, void* o,
                               hipStream_t st);
-// also writes lse2 = lse * log2(e) (the backward's exp2 argument offset)
+// also writes nd = -rowsum(dOg * Og) and nl = -lse / scale, the backward's
+// per-row offsets of dP and of the raw scores
 hipError_t launch_scatter_bwd(const LhGeom& g, int dtype, const void* dout, const float* og,
-                              const int32_t* gidx, const float* lse, void* dog, void* dogT, float* Dv,
-                              float* lse2, hipStream_t st);
+                              const int32_t* gidx, const float* lse, float scale, void* dog, void* dogT,
+                              float* nd, float* nl, hipStream_t st);
 hipError_t launch_gather_pool_bwd(const LhGeom& g, int dtype, const float* const dx_g[3], const int32_t* gpos,
                                   void* const dx[3], hipStream_t st);
 hipError_t launch_transpose(int dtype, int64_t BH, int64_t S, int64_t S_pad, int64_t d, const void* x,
                             void* xT, hipStream_t st);
 hipError_t launch_dense_bwd_prep(int dtype, int64_t BH, int64_t S, int64_t S_pad, int64_t d, const void* dout,
-                                 const float* o32, const float* lse, void* doT, float* Dv, float* lse2,
-                                 hipStream_t st);
+                                 const float* o32, const float* lse, float scale, void* doT, float* nd,
+                                 float* nl, hipStream_t st);
 
 // attention (lh_attention.hip)
 struct AttnArgs {
@@ -53,10 +54,10 @@ struct AttnArgs {
 // O32: f32 output [BH,S,d] (always); Ot: optional copy in the input dtype (may be null)
 hipError_t launch_attn_fwd(const AttnArgs& a, int dtype, const void* Q, const void* K, const void* VT, float* O32,
                            void* Ot, float* lse, hipStream_t st);
-// out_f32: dq/dk/dv are f32 (true) or the input dtype (false); lse2: log-sum-exp in log2 units
+// out_f32: dq/dk/dv are f32 (true) or the input dtype (false); nl = -LSE/scale, nd = -D per row
 hipError_t launch_attn_dkdv(const AttnArgs& a, int dtype, bool out_f32, const void* Q, const void* K,
-                            const void* V, const void* QT, const void* dO, const void* dOT, const float* lse,
-                            const float* Dv, void* dK, void* dV, hipStream_t st);
+                            const void* V, const void* QT, const void* dO, const void* dOT, const float* nl,
+                            const float* nd, void* dK, void* dV, hipStream_t st);
 hipError_t launch_attn_dq(const AttnArgs& a, int dtype, bool out_f32, const void* Q, const void* K, const void* V,
-                          const void* KT, const void* dO, const float* lse, const float* Dv, void* dQ,
+                          const void* KT, const void* dO, const float* nl, const float* nd, void* dQ,
                           hipStream_t st);

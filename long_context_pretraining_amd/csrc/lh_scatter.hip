@@ -166,9 +166,9 @@ template <typename T>
 __global__ __launch_bounds__(kThreads) void scatter_bwd_kernel(const T* __restrict__ dout,
                                                                const float* __restrict__ og,
                                                                const int32_t* __restrict__ gidx,
-                                                               const float* __restrict__ lse, T* dog, T* dogT,
-                                                               float* __restrict__ Dv, float* __restrict__ lse2,
-                                                               MapGeo G) {
+                                                               const float* __restrict__ lse, float inv_scale,
+                                                               T* dog, T* dogT, float* __restrict__ nd,
+                                                               float* __restrict__ nl, MapGeo G) {
     extern __shared__ __align__(16) unsigned char smem[];
     constexpr int VEC = V16<T>::N;
     typedef typename V16<T>::type VT;
@@ -248,8 +248,8 @@ __global__ __launch_bounds__(kThreads) void scatter_bwd_kernel(const T* __restri
         if (s < G.S) {
             float acc = 0.f;
             for (int vv = 0; vv < nvec; ++vv) acc += dpart[sl * nvec + vv];
-            Dv[bh * G.S + s] = acc;
-            lse2[bh * G.S + s] = lse[bh * G.S + s] * 1.4426950408889634f;
+            nd[bh * G.S + s] = -acc;
+            nl[bh * G.S + s] = -lse[bh * G.S + s] * inv_scale;
         }
     }
     store_transposed(tile, ld, G.d, dogT + bh * G.d * G.S_pad, G.S_pad, s0);
@@ -327,9 +327,10 @@ __global__ __launch_bounds__(kThreads) void transpose_kernel(const T* __restrict
 
 template <typename T>
 __global__ __launch_bounds__(kThreads) void dense_prep_kernel(const T* __restrict__ dout, const float* __restrict__ o,
-                                                              const float* __restrict__ lse, T* doT,
-                                                              float* __restrict__ Dv, float* __restrict__ lse2,
-                                                              int64_t S, int64_t S_pad, int64_t d) {
+                                                              const float* __restrict__ lse, float inv_scale,
+                                                              T* doT, float* __restrict__ nd,
+                                                              float* __restrict__ nl, int64_t S, int64_t S_pad,
+                                                              int64_t d) {
     extern __shared__ __align__(16) unsigned char smem[];
     constexpr int VEC = V16<T>::N;
     typedef typename V16<T>::type VT;
@@ -356,8 +357,8 @@ __global__ __launch_bounds__(kThreads) void dense_prep_kernel(const T* __restric
         if (s0 + sl < S) {
             float acc = 0.f;
             for (int vv = 0; vv < nvec; ++vv) acc += dpart[sl * nvec + vv];
-            Dv[bh * S + s0 + sl] = acc;
-            lse2[bh * S + s0 + sl] = lse[bh * S + s0 + sl] * 1.4426950408889634f;
+            nd[bh * S + s0 + sl] = -acc;
+            nl[bh * S + s0 + sl] = -lse[bh * S + s0 + sl] * inv_scale;
         }
     }
     store_transposed(tile, ld, d, doT + bh * d * S_pad, S_pad, s0);
@@ -396,17 +397,18 @@ hipError_t launch_scatter_fwd(const LhGeom& g, int dtype, const float* og, const
 }
 
 hipError_t launch_scatter_bwd(const LhGeom& g, int dtype, const void* dout, const float* og, const int32_t* gidx,
-                              const float* lse, void* dog, void* dogT, float* Dv, float* lse2, hipStream_t st) {
+                              const float* lse, float scale, void* dog, void* dogT, float* nd, float* nl,
+                              hipStream_t st) {
     const MapGeo G = make_geo(g);
     dim3 grid((unsigned)(g.S_pad / kRows), (unsigned)g.BH);
     if (dtype == LH_BF16) {
         const size_t sh = tile_bytes<bf16>(g.d) + 4 * kRows * (g.d / 8);
-        scatter_bwd_kernel<bf16><<<grid, kThreads, sh, st>>>((const bf16*)dout, og, gidx, lse, (bf16*)dog,
-                                                              (bf16*)dogT, Dv, lse2, G);
+        scatter_bwd_kernel<bf16><<<grid, kThreads, sh, st>>>((const bf16*)dout, og, gidx, lse, 1.f / scale,
+                                                              (bf16*)dog, (bf16*)dogT, nd, nl, G);
     } else {
         const size_t sh = tile_bytes<float>(g.d) + 4 * kRows * (g.d / 4);
-        scatter_bwd_kernel<float><<<grid, kThreads, sh, st>>>((const float*)dout, og, gidx, lse,
-                                                               (float*)dog, (float*)dogT, Dv, lse2, G);
+        scatter_bwd_kernel<float><<<grid, kThreads, sh, st>>>((const float*)dout, og, gidx, lse, 1.f / scale,
+                                                               (float*)dog, (float*)dogT, nd, nl, G);
     }
     return hipGetLastError();
 }
@@ -436,17 +438,17 @@ hipError_t launch_transpose(int dtype, int64_t BH, int64_t S, int64_t S_pad, int
 }
 
 hipError_t launch_dense_bwd_prep(int dtype, int64_t BH, int64_t S, int64_t S_pad, int64_t d, const void* dout,
-                                 const float* o, const float* lse, void* doT, float* Dv, float* lse2,
+                                 const float* o, const float* lse, float scale, void* doT, float* nd, float* nl,
                                  hipStream_t st) {
     dim3 grid((unsigned)(S_pad / kRows), (unsigned)BH);
     if (dtype == LH_BF16) {
         const size_t sh = tile_bytes<bf16>(d) + 4 * kRows * (d / 8);
-        dense_prep_kernel<bf16><<<grid, kThreads, sh, st>>>((const bf16*)dout, o, lse, (bf16*)doT, Dv, lse2,
-                                                             S, S_pad, d);
+        dense_prep_kernel<bf16><<<grid, kThreads, sh, st>>>((const bf16*)dout, o, lse, 1.f / scale, (bf16*)doT,
+                                                             nd, nl, S, S_pad, d);
     } else {
         const size_t sh = tile_bytes<float>(d) + 4 * kRows * (d / 4);
-        dense_prep_kernel<float><<<grid, kThreads, sh, st>>>((const float*)dout, o, lse, (float*)doT, Dv,
-                                                              lse2, S, S_pad, d);
+        dense_prep_kernel<float><<<grid, kThreads, sh, st>>>((const float*)dout, o, lse, 1.f / scale,
+                                                              (float*)doT, nd, nl, S, S_pad, d);
     }
     return hipGetLastError();
 }

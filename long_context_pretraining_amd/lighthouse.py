@@ -21,7 +21,7 @@ LH_F32, LH_BF16 = 0, 1
 LH_OK, LH_E_ARG, LH_E_UNSUPPORTED, LH_E_WORKSPACE, LH_E_DEVICE = 0, -1, -2, -3, -4
 MAX_LEVELS = 8
 FWD_QG, FWD_KG, FWD_VG, FWD_QT, FWD_KT, FWD_VT, FWD_O, FWD_LSE = range(8)
-BWD_DO, BWD_DOT, BWD_D, BWD_DQ, BWD_DK, BWD_DV, BWD_LSE2 = range(7)
+BWD_DO, BWD_DOT, BWD_NEG_D, BWD_DQ, BWD_DK, BWD_DV, BWD_NEG_LSE = range(7)
 
 DTYPE_CODE = {torch.float32: LH_F32, torch.bfloat16: LH_BF16}
 
