@@ -114,45 +114,133 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(const T* __restrict__ 
 }
 
 // ---------------------------------------------------------------------------
+// Pull kernels (scatter forward, gather + pool backward) over a block of R
+// tokens (a power of two chosen at launch so the staged rows fit in LDS).
+// Output token t reads the row of entry i_l(t) = floor((t + SHIFT) / p^l) -
+// SHIFT of every level l.  Coarse rows are shared by p^l consecutive tokens,
+// so the block stages them once: it loads the slot of every entry its tokens
+// read into LDS, then the f32 rows of the entries of levels >= 1 (zeros where
+// the entry is not selected).  Each token then reads its own level-0 row from
+// global memory (only if selected) and the coarser ones from LDS, and sums the
+// levels in ascending order.  L and the row width D are template parameters.
+// ---------------------------------------------------------------------------
+struct PullLds {
+    int R;          // tokens per block
+    int slot_cap;   // slots of all levels over R tokens
+    int row_cap;    // staged rows (levels >= 1)
+};
+
+inline PullLds pull_lds(int p, int L, int64_t d) {
+    PullLds P{};
+    for (int R = 256;; R /= 2) {
+        int slots = 0, rows = 0, q = 1;
+        for (int l = 0; l < L; ++l, q *= p) {
+            const int n = R / q + 2;
+            slots += n;
+            if (l > 0) rows += n;
+        }
+        P.R = R;
+        P.slot_cap = slots;
+        P.row_cap = rows;
+        if ((size_t)rows * d * 4 + (size_t)slots * 4 <= 40 * 1024 || R <= 16) return P;
+    }
+}
+
+template <int L, int D, int SHIFT>
+__device__ __forceinline__ void stage_block_rows(const MapGeo& G, const int32_t* gp, const float* rows_g, int64_t t0,
+                                                 int64_t t1, int32_t* slot, float* rows, int64_t* lo, int* base) {
+    int n[L];
+    int acc = 0;
+#pragma unroll
+    for (int l = 0; l < L; ++l) {
+        lo[l] = (int64_t)div_pw(G, l, (uint32_t)(t0 + SHIFT)) - SHIFT;
+        const int64_t hi = (int64_t)div_pw(G, l, (uint32_t)(t1 + SHIFT)) - SHIFT;
+        base[l] = acc;
+        n[l] = (int)(hi - lo[l] + 1);
+        acc += n[l];
+    }
+    // slots of every level (-1 outside [0, M_l))
+#pragma unroll
+    for (int l = 0; l < L; ++l) {
+        const int64_t M = G.off[l + 1] - G.off[l];
+        for (int j = threadIdx.x; j < n[l]; j += kThreads) {
+            const int64_t i = lo[l] + j;
+            slot[base[l] + j] = (i >= 0 && i < M) ? gp[G.off[l] + i] : -1;
+        }
+    }
+    __syncthreads();
+    // rows of levels >= 1: staged entry e is slot n_0 + e
+    constexpr int CH = D / 4;   // 16-byte chunks per row
+    const int ne = acc - n[0];
+    constexpr int BATCH = 8;   // loads in flight per thread
+    for (int t0_ = threadIdx.x; t0_ < ne * CH; t0_ += BATCH * kThreads) {
+        floatx4 v[BATCH];
+#pragma unroll
+        for (int u = 0; u < BATCH; ++u) {
+            const int task = t0_ + u * kThreads;
+            const int e = task / CH, c = task - e * CH;
+            const int32_t g = task < ne * CH ? slot[n[0] + e] : -1;
+            v[u] = floatx4{};
+            if (g >= 0 && g < G.S) v[u] = *reinterpret_cast<const floatx4*>(rows_g + (int64_t)g * D + 4 * c);
+        }
+#pragma unroll
+        for (int u = 0; u < BATCH; ++u) {
+            const int task = t0_ + u * kThreads;
+            if (task < ne * CH) *reinterpret_cast<floatx4*>(rows + task * 4) = v[u];
+        }
+    }
+    __syncthreads();
+}
+
+// x[l] = the 8 f32 elements vv*8 .. vv*8+7 of token t's level-l row (zeros
+// where the entry is not selected).
+template <int L, int D, int SHIFT>
+__device__ __forceinline__ void pull_token(const MapGeo& G, const float* rows_g, const int32_t* slot,
+                                           const float* rows, const int64_t* lo, const int* base, int64_t t, int vv,
+                                           floatx8* x) {
+    const int32_t g0 = slot[(int)(t - lo[0])];   // level 0: i_0(t) = t
+    x[0] = floatx8{};
+    if (g0 >= 0 && g0 < G.S) x[0] = *reinterpret_cast<const floatx8*>(rows_g + (int64_t)g0 * D + vv * 8);
+#pragma unroll
+    for (int l = 1; l < L; ++l) {
+        const int e = base[l] - base[1] + (int)((int64_t)div_pw(G, l, (uint32_t)(t + SHIFT)) - SHIFT - lo[l]);
+        x[l] = *reinterpret_cast<const floatx8*>(rows + e * D + vv * 8);
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Scatter forward (pull): o[t] = sum_l Og[gpos(l, floor((t+1)/p^l) - 1)],
 // levels ascending, in f32 from the f32 sub-sequence output, one rounding to
 // T; 0 where no selected entry covers t.
 // ---------------------------------------------------------------------------
-template <typename T>
+template <typename T, int L, int D>
 __global__ __launch_bounds__(kThreads) void scatter_fwd_kernel(const float* __restrict__ og,
                                                                const int32_t* __restrict__ gpos,
-                                                               T* __restrict__ o, MapGeo G) {
+                                                               T* __restrict__ o, MapGeo G, PullLds P) {
     typedef typename Frag<T>::type OV;
-    const int64_t bh = blockIdx.y, t0 = (int64_t)blockIdx.x * kRows;
-    const int nvec = (int)(G.d / 8);
-    const int32_t* gp = gpos + bh * G.M_total;
-    for (int task = threadIdx.x; task < kRows * nvec; task += kThreads) {
-        const int tl = task / nvec, vv = task - tl * nvec;
+    constexpr int NVEC = D / 8;
+    extern __shared__ __align__(16) unsigned char smem[];
+    float* rows = reinterpret_cast<float*>(smem);
+    int32_t* slot = reinterpret_cast<int32_t*>(smem + (size_t)P.row_cap * D * 4);
+    const int64_t bh = blockIdx.y, t0 = (int64_t)blockIdx.x * P.R;
+    const int64_t t1 = (t0 + P.R < G.N ? t0 + P.R : G.N) - 1;
+    const float* ogh = og + bh * G.S * D;
+    int64_t lo[L];
+    int base[L];
+    stage_block_rows<L, D, 1>(G, gpos + bh * G.M_total, ogh, t0, t1, slot, rows, lo, base);
+    const int ntask = (int)(t1 - t0 + 1) * NVEC;
+    for (int task = threadIdx.x; task < ntask; task += kThreads) {
+        const int tl = task / NVEC, vv = task - tl * NVEC;
         const int64_t t = t0 + tl;
-        if (t >= G.N) continue;
-        // all levels' slot lookups first, then all row loads: independent memory operations
-        int32_t gl[LH_MAX_LEVELS];
-#pragma unroll
-        for (int l = 0; l < LH_MAX_LEVELS; ++l) {
-            gl[l] = -1;
-            if (l < G.L) {
-                const uint32_t i1 = div_pw(G, l, (uint32_t)(t + 1));
-                if (i1 > 0) gl[l] = gp[G.off[l] + i1 - 1];
-            }
-        }
-        floatx8 x[LH_MAX_LEVELS];
-#pragma unroll
-        for (int l = 0; l < LH_MAX_LEVELS; ++l) {
-            x[l] = floatx8{};
-            if (gl[l] >= 0 && gl[l] < G.S) x[l] = *reinterpret_cast<const floatx8*>(og + (bh * G.S + gl[l]) * G.d + vv * 8);
-        }
+        floatx8 x[L];
+        pull_token<L, D, 1>(G, ogh, slot, rows, lo, base, t, vv, x);
         floatx8 acc = x[0];
 #pragma unroll
-        for (int l = 1; l < LH_MAX_LEVELS; ++l) acc += x[l];
+        for (int l = 1; l < L; ++l) acc += x[l];
         OV out;
 #pragma unroll
         for (int e = 0; e < 8; ++e) out[e] = static_cast<T>(acc[e]);
-        *reinterpret_cast<OV*>(o + (bh * G.N + t) * G.d + vv * 8) = out;
+        *reinterpret_cast<OV*>(o + (bh * G.N + t) * D + vv * 8) = out;
     }
 }
 
@@ -259,45 +347,42 @@ __global__ __launch_bounds__(kThreads) void scatter_bwd_kernel(const T* __restri
 // Gather + pooling backward (pull): dX[t] = sum_l dXg[gpos(l, floor(t/p^l))] / p^l
 // over selected entries, levels ascending, f32, stored in T.
 // ---------------------------------------------------------------------------
-template <typename T>
+template <typename T, int L, int D>
 __global__ __launch_bounds__(kThreads) void gpool_bwd_kernel(const float* __restrict__ g0,
                                                              const float* __restrict__ g1,
                                                              const float* __restrict__ g2,
                                                              const int32_t* __restrict__ gpos, T* o0, T* o1, T* o2,
-                                                             MapGeo G) {
+                                                             MapGeo G, PullLds P) {
+    typedef typename Frag<T>::type OV;
+    constexpr int NVEC = D / 8;
+    extern __shared__ __align__(16) unsigned char smem[];
+    float* rows = reinterpret_cast<float*>(smem);
+    int32_t* slot = reinterpret_cast<int32_t*>(smem + (size_t)P.row_cap * D * 4);
     const int z = blockIdx.z;
-    const float* dxg = z == 0 ? g0 : (z == 1 ? g1 : g2);
+    const float* dxg = (z == 0 ? g0 : (z == 1 ? g1 : g2)) + (int64_t)blockIdx.y * G.S * D;
     T* out = z == 0 ? o0 : (z == 1 ? o1 : o2);
-    const int64_t bh = blockIdx.y, t0 = (int64_t)blockIdx.x * kRows;
-    const int nvec = (int)(G.d / 8);
-    const int32_t* gp = gpos + bh * G.M_total;
-    for (int task = threadIdx.x; task < kRows * nvec; task += kThreads) {
-        const int tl = task / nvec, vv = task - tl * nvec;
+    const int64_t bh = blockIdx.y, t0 = (int64_t)blockIdx.x * P.R;
+    const int64_t t1 = (t0 + P.R < G.N ? t0 + P.R : G.N) - 1;
+    int64_t lo[L];
+    int base[L];
+    stage_block_rows<L, D, 0>(G, gpos + bh * G.M_total, dxg, t0, t1, slot, rows, lo, base);
+    const int ntask = (int)(t1 - t0 + 1) * NVEC;
+    for (int task = threadIdx.x; task < ntask; task += kThreads) {
+        const int tl = task / NVEC, vv = task - tl * NVEC;
         const int64_t t = t0 + tl;
-        if (t >= G.N) continue;
-        // all levels' slot lookups first, then all row loads: independent memory operations
-        int32_t gl[LH_MAX_LEVELS];
-#pragma unroll
-        for (int l = 0; l < LH_MAX_LEVELS; ++l) gl[l] = l < G.L ? gp[G.off[l] + div_pw(G, l, (uint32_t)t)] : -1;
-        floatx8 x[LH_MAX_LEVELS];
-#pragma unroll
-        for (int l = 0; l < LH_MAX_LEVELS; ++l) {
-            x[l] = floatx8{};
-            if (gl[l] >= 0 && gl[l] < G.S) x[l] = *reinterpret_cast<const floatx8*>(dxg + (bh * G.S + gl[l]) * G.d + vv * 8);
-        }
+        floatx8 x[L];
+        pull_token<L, D, 0>(G, dxg, slot, rows, lo, base, t, vv, x);
         float acc[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[e] = 0.f;
 #pragma unroll
-        for (int l = 0; l < LH_MAX_LEVELS; ++l) {
-            const float w = l < G.L ? G.inv[l] : 0.f;
+        for (int l = 0; l < L; ++l)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) acc[e] = fmaf(x[l][e], w, acc[e]);
-        }
-        typename Frag<T>::type r;
+            for (int e = 0; e < 8; ++e) acc[e] = fmaf(x[l][e], G.inv[l], acc[e]);
+        OV r;
 #pragma unroll
         for (int e = 0; e < 8; ++e) r[e] = static_cast<T>(acc[e]);
-        *reinterpret_cast<typename Frag<T>::type*>(out + (bh * G.N + t) * G.d + vv * 8) = r;
+        *reinterpret_cast<OV*>(out + (bh * G.N + t) * D + vv * 8) = r;
     }
 }
 
@@ -385,15 +470,33 @@ hipError_t launch_gather(const LhGeom& g, int dtype, const void* q, const void* 
     return hipGetLastError();
 }
 
+// Calls f.template operator()<L, D>() for the runtime level count and row width.
+template <class F>
+hipError_t with_levels(int L, int64_t d, F&& f) {
+    if (d != 64 && d != 128) return hipErrorInvalidValue;
+#define LH_LD(l)                                                                       \
+    case l:                                                                            \
+        return d == 64 ? f.template operator()<l, 64>() : f.template operator()<l, 128>();
+    switch (L) {
+        LH_LD(1) LH_LD(2) LH_LD(3) LH_LD(4) LH_LD(5) LH_LD(6) LH_LD(7) LH_LD(8)
+        default: return hipErrorInvalidValue;
+    }
+#undef LH_LD
+}
+
 hipError_t launch_scatter_fwd(const LhGeom& g, int dtype, const float* og, const int32_t* gpos, void* o,
                               hipStream_t st) {
     const MapGeo G = make_geo(g);
-    dim3 grid(blocks_for(g.N), (unsigned)g.BH);
-    if (dtype == LH_BF16)
-        scatter_fwd_kernel<bf16><<<grid, kThreads, 0, st>>>(og, gpos, (bf16*)o, G);
-    else
-        scatter_fwd_kernel<float><<<grid, kThreads, 0, st>>>(og, gpos, (float*)o, G);
-    return hipGetLastError();
+    const PullLds P = pull_lds(g.p, g.L, g.d);
+    dim3 grid((unsigned)((g.N + P.R - 1) / P.R), (unsigned)g.BH);
+    const size_t sh = (size_t)P.row_cap * g.d * 4 + (size_t)P.slot_cap * 4;
+    return with_levels(g.L, g.d, [&]<int L, int D>() {
+        if (dtype == LH_BF16)
+            scatter_fwd_kernel<bf16, L, D><<<grid, kThreads, sh, st>>>(og, gpos, (bf16*)o, G, P);
+        else
+            scatter_fwd_kernel<float, L, D><<<grid, kThreads, sh, st>>>(og, gpos, (float*)o, G, P);
+        return hipGetLastError();
+    });
 }
 
 hipError_t launch_scatter_bwd(const LhGeom& g, int dtype, const void* dout, const float* og, const int32_t* gidx,
@@ -416,14 +519,19 @@ hipError_t launch_scatter_bwd(const LhGeom& g, int dtype, const void* dout, cons
 hipError_t launch_gather_pool_bwd(const LhGeom& g, int dtype, const float* const dx_g[3], const int32_t* gpos,
                                   void* const dx[3], hipStream_t st) {
     const MapGeo G = make_geo(g);
-    dim3 grid(blocks_for(g.N), (unsigned)g.BH, 3);
-    if (dtype == LH_BF16)
-        gpool_bwd_kernel<bf16><<<grid, kThreads, 0, st>>>(dx_g[0], dx_g[1], dx_g[2], gpos, (bf16*)dx[0],
-                                                          (bf16*)dx[1], (bf16*)dx[2], G);
-    else
-        gpool_bwd_kernel<float><<<grid, kThreads, 0, st>>>(dx_g[0], dx_g[1], dx_g[2], gpos, (float*)dx[0],
-                                                           (float*)dx[1], (float*)dx[2], G);
-    return hipGetLastError();
+    const PullLds P = pull_lds(g.p, g.L, g.d);
+    dim3 grid((unsigned)((g.N + P.R - 1) / P.R), (unsigned)g.BH, 3);
+    const size_t sh = (size_t)P.row_cap * g.d * 4 + (size_t)P.slot_cap * 4;
+    return with_levels(g.L, g.d, [&]<int L, int D>() {
+        if (dtype == LH_BF16)
+            gpool_bwd_kernel<bf16, L, D><<<grid, kThreads, sh, st>>>(dx_g[0], dx_g[1], dx_g[2], gpos, (bf16*)dx[0],
+                                                                     (bf16*)dx[1], (bf16*)dx[2], G, P);
+        else
+            gpool_bwd_kernel<float, L, D><<<grid, kThreads, sh, st>>>(dx_g[0], dx_g[1], dx_g[2], gpos,
+                                                                      (float*)dx[0], (float*)dx[1], (float*)dx[2], G,
+                                                                      P);
+        return hipGetLastError();
+    });
 }
 
 hipError_t launch_transpose(int dtype, int64_t BH, int64_t S, int64_t S_pad, int64_t d, const void* x, void* xT,
