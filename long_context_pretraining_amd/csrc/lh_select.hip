@@ -21,9 +21,9 @@ constexpr int kThreads = 256;
 // ---------------------------------------------------------------------------
 struct PoolP {
     int64_t N, d, BH, Mu;
-    int p, L, chunk, DS, nslices;
+    int p, L, chunk, DS, nslices, nv_log2;   // DS / VEC = 1 << nv_log2 vectors per row slice
     int64_t offu[LH_MAX_LEVELS];  // row of level l inside a head's pyramid block
-    int64_t pw[LH_MAX_LEVELS];
+    int epc[LH_MAX_LEVELS];       // entries of level l per chunk (chunk / p^l)
 };
 
 template <typename T>
@@ -34,34 +34,79 @@ __global__ __launch_bounds__(kThreads) void pool_kernel(const T* __restrict__ x0
     typedef typename V16<T>::type VT;
     const T* x = blockIdx.z == 0 ? x0 : (blockIdx.z == 1 ? x1 : x2);
     const int slice = blockIdx.x % P.nslices;
-    const int64_t c0 = (int64_t)(blockIdx.x / P.nslices) * P.chunk;
-    const int64_t len = (P.N - c0) < P.chunk ? (P.N - c0) : P.chunk;
+    const int cidx = blockIdx.x / P.nslices;
+    const int64_t c0 = (int64_t)cidx * P.chunk;
+    const int len = (int)((P.N - c0) < P.chunk ? (P.N - c0) : P.chunk);
     const int64_t bh = blockIdx.y;
     const int dim0 = slice * P.DS;
-    const int nvec = P.DS / VEC;
+    const int nvm = (1 << P.nv_log2) - 1;
     const T* xh = x + bh * P.N * P.d;
     T* ph = pyr + ((int64_t)blockIdx.z * P.BH + bh) * P.Mu * P.d;
 
-    int prev_off = 0, cur_off = 0;
-    int64_t n_prev = len;
-    for (int l = 1; l < P.L; ++l) {
-        const int n = (int)(n_prev / P.p);
-        const int64_t e0 = c0 / P.pw[l];
-        for (int task = threadIdx.x; task < n * nvec; task += kThreads) {
-            const int e = task / nvec, vv = task - e * nvec;
+    // Level 1 from the input: two entries per step, every child load issued
+    // before any is summed (children summed in index order, then / p).
+    const int n1 = len / P.p;
+    const int nt = n1 << P.nv_log2;
+    for (int ta = threadIdx.x; ta < nt; ta += 2 * kThreads) {
+        int task[2] = {ta, ta + kThreads};
+        float acc[2][VEC];
+        const T* src[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int tk = task[j] < nt ? task[j] : ta;
+            src[j] = xh + (c0 + (int64_t)(tk >> P.nv_log2) * P.p) * P.d + dim0 + (tk & nvm) * VEC;
+#pragma unroll
+            for (int i = 0; i < VEC; ++i) acc[j][i] = 0.f;
+        }
+        for (int cb = 0; cb < P.p; cb += 4) {
+            VT v[2][4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    v[j][u] = VT{};
+                    if (cb + u < P.p) v[j][u] = *reinterpret_cast<const VT*>(src[j] + (int64_t)(cb + u) * P.d);
+                }
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                if (cb + u < P.p)
+#pragma unroll
+                    for (int j = 0; j < 2; ++j)
+#pragma unroll
+                        for (int i = 0; i < VEC; ++i) acc[j][i] += to_f(v[j][u][i]);
+        }
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            if (task[j] >= nt) continue;
+            const int e = task[j] >> P.nv_log2, vv = task[j] & nvm;
+            VT out;
+#pragma unroll
+            for (int i = 0; i < VEC; ++i) {
+                acc[j][i] = acc[j][i] / (float)P.p;
+                out[i] = static_cast<T>(acc[j][i]);
+            }
+            if (P.L > 2) {
+                float* dst = lds + e * P.DS + vv * VEC;
+#pragma unroll
+                for (int i = 0; i < VEC; ++i) dst[i] = acc[j][i];
+            }
+            *reinterpret_cast<VT*>(ph + (P.offu[1] + (int64_t)cidx * P.epc[1] + e) * P.d + dim0 + vv * VEC) = out;
+        }
+    }
+    __syncthreads();
+    // Levels 2 .. L-1 from the f32 level below, kept in LDS.
+    int prev_off = 0, cur_off = n1 * P.DS, n_prev = n1;
+    for (int l = 2; l < P.L; ++l) {
+        const int n = n_prev / P.p;
+        for (int task = threadIdx.x; task < (n << P.nv_log2); task += kThreads) {
+            const int e = task >> P.nv_log2, vv = task & nvm;
             float acc[VEC];
 #pragma unroll
             for (int i = 0; i < VEC; ++i) acc[i] = 0.f;
             for (int c = 0; c < P.p; ++c) {
-                if (l == 1) {
-                    const VT v = *reinterpret_cast<const VT*>(xh + (c0 + (int64_t)e * P.p + c) * P.d + dim0 + vv * VEC);
+                const float* src = lds + prev_off + (e * P.p + c) * P.DS + vv * VEC;
 #pragma unroll
-                    for (int i = 0; i < VEC; ++i) acc[i] += to_f(v[i]);
-                } else {
-                    const float* src = lds + prev_off + (e * P.p + c) * P.DS + vv * VEC;
-#pragma unroll
-                    for (int i = 0; i < VEC; ++i) acc[i] += src[i];
-                }
+                for (int i = 0; i < VEC; ++i) acc[i] += src[i];
             }
             VT out;
 #pragma unroll
@@ -74,7 +119,7 @@ __global__ __launch_bounds__(kThreads) void pool_kernel(const T* __restrict__ x0
 #pragma unroll
                 for (int i = 0; i < VEC; ++i) dst[i] = acc[i];
             }
-            *reinterpret_cast<VT*>(ph + (P.offu[l] + e0 + e) * P.d + dim0 + vv * VEC) = out;
+            *reinterpret_cast<VT*>(ph + (P.offu[l] + (int64_t)cidx * P.epc[l] + e) * P.d + dim0 + vv * VEC) = out;
         }
         __syncthreads();
         prev_off = cur_off;
@@ -94,16 +139,17 @@ struct ScoreP {
     int64_t N, d, BH, Mu;
     int p, L, chunk;
     int64_t offu[LH_MAX_LEVELS];
-    int64_t pw[LH_MAX_LEVELS];
+    int epc[LH_MAX_LEVELS];   // entries of level l per chunk (chunk / p^l)
 };
 
-template <typename T>
-__device__ __forceinline__ float sumsq_lane(const T* __restrict__ row, int cw) {
+template <typename T, int CW>
+__device__ __forceinline__ float sumsq_lane(const T* __restrict__ row) {
 #pragma clang fp contract(off)
     constexpr int VEC = V16<T>::N;
     typedef typename V16<T>::type VT;
     float a = 0.f;
-    for (int j = 0; j < cw; j += VEC) {
+#pragma unroll
+    for (int j = 0; j < CW; j += VEC) {
         const VT v = *reinterpret_cast<const VT*>(row + j);
 #pragma unroll
         for (int i = 0; i < VEC; ++i) {
@@ -122,7 +168,7 @@ __device__ __forceinline__ float tree8(float a) {
     return u + __shfl_xor(u, 1, 64);
 }
 
-template <typename T>
+template <typename T, int D>
 __global__ __launch_bounds__(kThreads) void score_kernel(const T* __restrict__ q, const T* __restrict__ k,
                                                          float* __restrict__ sigma, ScoreP P) {
 #pragma clang fp contract(off)
@@ -130,12 +176,12 @@ __global__ __launch_bounds__(kThreads) void score_kernel(const T* __restrict__ q
     const int64_t bh = blockIdx.y;
     const int64_t c0 = (int64_t)blockIdx.x * P.chunk;
     const int len = (int)((P.N - c0) < P.chunk ? (P.N - c0) : P.chunk);
-    const int cw = (int)(P.d / 8);
+    constexpr int CW = D / 8;
     const int r = threadIdx.x & 7;
     for (int tok = threadIdx.x >> 3; tok < len; tok += kThreads / 8) {
-        const int64_t row = (bh * P.N + c0 + tok) * P.d + r * cw;
-        const float sq = tree8(sumsq_lane(q + row, cw));
-        const float sk = tree8(sumsq_lane(k + row, cw));
+        const int64_t row = (bh * P.N + c0 + tok) * D + r * CW;
+        const float sq = tree8(sumsq_lane<T, CW>(q + row));
+        const float sk = tree8(sumsq_lane<T, CW>(k + row));
         if (r == 0) lds[tok] = sqrtf(sq) + sqrtf(sk);
     }
     __syncthreads();
@@ -144,7 +190,7 @@ __global__ __launch_bounds__(kThreads) void score_kernel(const T* __restrict__ q
     float* sg = sigma + bh * P.Mu;
     for (int l = 1; l < P.L; ++l) {
         const int n = n_prev / P.p;
-        const int64_t e0 = c0 / P.pw[l];
+        const int64_t e0 = (int64_t)blockIdx.x * P.epc[l];
         for (int e = threadIdx.x; e < n; e += kThreads) {
             float m = lds[prev_off + e * P.p];
             for (int c = 1; c < P.p; ++c) m = fmaxf(m, lds[prev_off + e * P.p + c]);
@@ -375,7 +421,7 @@ hipError_t launch_pool(const LhGeom& g, int dtype, const void* q, const void* k,
     if (g.L < 2) return hipSuccess;
     PoolP P{};
     P.N = g.N; P.d = g.d; P.BH = g.BH; P.Mu = g.Mu; P.p = g.p; P.L = g.L;
-    for (int l = 0; l < g.L; ++l) { P.offu[l] = l ? g.off[l] - g.N : 0; P.pw[l] = g.pw[l]; }
+    for (int l = 0; l < g.L; ++l) P.offu[l] = l ? g.off[l] - g.N : 0;
     const int VEC = dtype == LH_BF16 ? 8 : 4;
     int64_t chunk = g.pw[g.L - 1];
     while (chunk < 256 && chunk * 2 <= g.N) chunk *= 2;
@@ -390,6 +436,9 @@ hipError_t launch_pool(const LhGeom& g, int dtype, const void* q, const void* k,
     while (lds_bytes(chunk, DS) > 48 * 1024 && DS > VEC) DS /= 2;
     if (lds_bytes(chunk, DS) > 64 * 1024) return hipErrorInvalidValue;
     P.chunk = (int)chunk; P.DS = DS; P.nslices = (int)(g.d / DS);
+    while ((VEC << P.nv_log2) < DS) ++P.nv_log2;
+    if ((VEC << P.nv_log2) != DS) return hipErrorInvalidValue;
+    for (int l = 0; l < g.L; ++l) P.epc[l] = (int)(chunk / g.pw[l]);
     dim3 grid((unsigned)(ceil_div(g.N, chunk) * P.nslices), (unsigned)g.BH, 3);
     size_t sh = (size_t)lds_bytes(chunk, DS);
     if (dtype == LH_BF16)
@@ -403,18 +452,23 @@ hipError_t launch_scores(const LhGeom& g, int dtype, const void* q, const void* 
     if (g.L < 2) return hipSuccess;
     ScoreP P{};
     P.N = g.N; P.d = g.d; P.BH = g.BH; P.Mu = g.Mu; P.p = g.p; P.L = g.L;
-    for (int l = 0; l < g.L; ++l) { P.offu[l] = l ? g.off[l] - g.N : 0; P.pw[l] = g.pw[l]; }
+    for (int l = 0; l < g.L; ++l) P.offu[l] = l ? g.off[l] - g.N : 0;
     int64_t chunk = g.pw[g.L - 1];
     while (chunk < 1024 && chunk * 2 <= g.N) chunk *= 2;
     if (chunk > 16384) return hipErrorInvalidValue;
     P.chunk = (int)chunk;
+    for (int l = 0; l < g.L; ++l) P.epc[l] = (int)(chunk / g.pw[l]);
     int64_t ent = chunk;
     for (int l = 1; l < g.L; ++l) ent += chunk / g.pw[l];
     dim3 grid((unsigned)ceil_div(g.N, chunk), (unsigned)g.BH);
-    if (dtype == LH_BF16)
-        score_kernel<bf16><<<grid, kThreads, ent * 4, st>>>((const bf16*)q, (const bf16*)k, sigma, P);
-    else
-        score_kernel<float><<<grid, kThreads, ent * 4, st>>>((const float*)q, (const float*)k, sigma, P);
+    if (g.d != 64 && g.d != 128) return hipErrorInvalidValue;
+    if (dtype == LH_BF16) {
+        if (g.d == 64) score_kernel<bf16, 64><<<grid, kThreads, ent * 4, st>>>((const bf16*)q, (const bf16*)k, sigma, P);
+        else score_kernel<bf16, 128><<<grid, kThreads, ent * 4, st>>>((const bf16*)q, (const bf16*)k, sigma, P);
+    } else {
+        if (g.d == 64) score_kernel<float, 64><<<grid, kThreads, ent * 4, st>>>((const float*)q, (const float*)k, sigma, P);
+        else score_kernel<float, 128><<<grid, kThreads, ent * 4, st>>>((const float*)q, (const float*)k, sigma, P);
+    }
     return hipGetLastError();
 }
 
