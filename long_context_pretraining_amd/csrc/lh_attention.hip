@@ -266,8 +266,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const T* __restri
 #pragma unroll
                 for (int c2 = 0; c2 < 2; ++c2) {
                     F p0, p1, r0, r1;
-                    split_frag<T>(s[ks][0], c2, p0, r0);
-                    split_frag<T>(s[ks][1], c2, p1, r1);
+                    split_frag_vec<T>(s[ks][0], c2, p0, r0);
+                    split_frag_vec<T>(s[ks][1], c2, p1, r1);
 #pragma unroll
                     for (int db = 0; db < D / 32; ++db) {
                         const F vf = tile_frag<T, VROWB>(lv, 32 * db + col, 32 * ks + 16 * c2 + 8 * h);

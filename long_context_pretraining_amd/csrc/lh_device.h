@@ -117,6 +117,30 @@ __device__ __forceinline__ void split_frag<float>(const floatx16& c, int cc, flo
     lo = hi;
 }
 
+// The same split with x - hi from a shift or mask of the packed pair and a
+// subtraction (bit-identical results): plain vector operations, which the
+// hardware issues alongside matrix products, where the dot2 form is not.
+template <typename T>
+__device__ __forceinline__ void split_frag_vec(const floatx16& c, int cc, typename Frag<T>::type& hi,
+                                               typename Frag<T>::type& lo) {
+    split_frag<T>(c, cc, hi, lo);
+}
+template <>
+__device__ __forceinline__ void split_frag_vec<bf16>(const floatx16& c, int cc, bf16x8& hi, bf16x8& lo) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const float x0 = c[8 * cc + 2 * e], x1 = c[8 * cc + 2 * e + 1];
+        const bf16x2 h = __builtin_convertvector((floatx2){x0, x1}, bf16x2);
+        const uint32_t hb = __builtin_bit_cast(uint32_t, h);
+        const float r0 = x0 - __uint_as_float(hb << 16), r1 = x1 - __uint_as_float(hb & 0xffff0000u);
+        const bf16x2 l = __builtin_convertvector((floatx2){r0, r1}, bf16x2);
+        hi[2 * e] = h[0];
+        hi[2 * e + 1] = h[1];
+        lo[2 * e] = l[0];
+        lo[2 * e + 1] = l[1];
+    }
+}
+
 // max over the 16 registers of a C tile (eight 3-input maxima)
 __device__ __forceinline__ float max16(const floatx16& v) {
     float m = __builtin_fmaxf(v[0], v[1]);
