@@ -8,9 +8,11 @@ selection is recomputed every step, as in training.  The workload is the
 (B=1, H=16, N=98304, d=64, bf16, p=4, L=4; S = 19968).
 
 Prints ONE JSON line: tokens/s of the layer (B*N per step), the dense causal
-attention baseline on the same GPU and inputs (speedup), the roofline of the
-dominant kernel measured live with HIP events on the library's stream, and
-the CPU oracle timed on a bounded sample.
+attention baseline on the same GPU and inputs (speedup, fwd+bwd and forward
+only), the roofline of the dominant kernel measured live with HIP events on
+the library's stream, and the CPU oracle timed on a bounded sample.  Other
+workloads of the parity suite can be timed with --workload NAME (their lines
+are reported alongside, never as the headline value).
 
     python bench.py [--steps K] [--warmup W] [--gpus 1]
 """
@@ -291,16 +293,22 @@ def main():
         lh.dense_causal_attn(ddesc, qd, kd, vd, o, lse, dws)
         lh.dense_causal_attn_backward(ddesc, qd, kd, vd, lse, dws, dod, dq, dk, dv, dwsb)
 
-    dense_ms = None
-    if args.dense_steps > 0:
-        dense_step()
+    def timed(fn, n):
+        fn()
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        for _ in range(args.dense_steps):
-            dense_step()
+        for _ in range(n):
+            fn()
         torch.cuda.synchronize()
-        dense_ms = (time.perf_counter() - t0) * 1e3 / args.dense_steps
+        return (time.perf_counter() - t0) * 1e3 / n
+
+    dense_ms = dense_fwd_ms = None
+    if args.dense_steps > 0:
+        dense_ms = timed(dense_step, args.dense_steps)
+        dense_fwd_ms = timed(lambda: lh.dense_causal_attn(ddesc, qd, kd, vd, o, lse, dws), args.dense_steps)
     del dws, dwsb
+    # forward only (selection included), after the timed region
+    fwd_ms = timed(lambda: layer.forward(qd, kd, vd, o), args.steps)
 
     if args.calibration_copy:   # a plain copy kernel of known size: reads and writes 1 GiB
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -309,8 +317,10 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    headline = args.workload == "llama530m_98k_k1536"
     out = {
-        "metric": "Lighthouse fwd+bwd tokens/s at N=98K,k=1536; speedup vs dense causal attn",
+        "metric": ("Lighthouse fwd+bwd tokens/s at N=98K,k=1536; speedup vs dense causal attn" if headline
+                   else f"Lighthouse fwd+bwd tokens/s, workload {w.name}; speedup vs dense causal attn"),
         "value": round(tokens_per_s, 1),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -327,6 +337,9 @@ def main():
         "speedup_vs_dense": round(dense_ms / ms_step, 3) if dense_ms else None,
         "dense_ms_per_step": round(dense_ms, 3) if dense_ms else None,
         "dense_tokens_per_s": round(w.B * w.N / (dense_ms * 1e-3), 1) if dense_ms else None,
+        "fwd_ms": round(fwd_ms, 4),
+        "dense_fwd_ms": round(dense_fwd_ms, 3) if dense_fwd_ms else None,
+        "speedup_fwd_vs_dense": round(dense_fwd_ms / fwd_ms, 3) if dense_fwd_ms else None,
         "kernel_ms": {n: round(x, 4) for n, x in kernel_ms.items()},
         "roofline": roof,
     }

@@ -32,6 +32,11 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kDkdvNW = 8;      // waves per dK/dV block (32 keys each; d = 128: 4)
 
+// Blocks per CU the forward and dQ kernels are built for: two (two waves per
+// SIMD) where a wave's registers fit in 256, one for d = 128, whose
+// accumulators and fragments need the whole register file of a SIMD.
+template <typename T, int D> constexpr int kBlocksPerCu = D * (int)sizeof(T) > 128 ? 1 : 2;
+
 struct AttnK {
     int64_t BH, S, S_pad;
     float scale, scale_log2;
@@ -142,7 +147,7 @@ template <typename T> constexpr bool kSplitP = sizeof(T) == 2;
 // The output is written in f32 (and, when Ot is given, also in T).
 // ---------------------------------------------------------------------------
 template <typename T, int D>
-__global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K,
+__global__ __launch_bounds__(kThreads, (kBlocksPerCu<T, D>)) void attn_fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K,
                                                             const T* __restrict__ VT, float* __restrict__ O32,
                                                             T* __restrict__ Ot, float* __restrict__ LSE, AttnK a) {
     typedef typename Frag<T>::type F;
@@ -319,7 +324,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const T* __restri
 // noise.  bf16 therefore feeds dS as hi + lo parts (as P in the forward).
 // ---------------------------------------------------------------------------
 template <typename T, int D, typename OutT>
-__global__ __launch_bounds__(kThreads, 2) void attn_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K,
+__global__ __launch_bounds__(kThreads, (kBlocksPerCu<T, D>)) void attn_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K,
                                                            const T* __restrict__ V, const T* __restrict__ KT,
                                                            const T* __restrict__ dO, const float* __restrict__ NL,
                                                            const float* __restrict__ ND, OutT* __restrict__ dQ,
