@@ -57,6 +57,9 @@ WORKLOADS = {
     # Same shapes with clustered high-norm spans and exact ties (built in tests).
     "llama530m_98k_adversarial": Workload("llama530m_98k_adversarial", 1, 16, 98304, 64, "bf16", 4, 4, 1536, 4, True),
     "extreme_512k": Workload("extreme_512k", 1, 16, 524288, 64, "bf16", 4, 6, 1536, 5, True),
+    # The ablation optimum of the technical summary (Experimental Results): p = 2, L = 3, k = 1536,
+    # on the same 98K layer (S = 30720).
+    "ablation_p2_L3_98k": Workload("ablation_p2_L3_98k", 1, 16, 98304, 64, "bf16", 2, 3, 1536, 6, True),
 }
 
 TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16}

@@ -55,3 +55,8 @@ def test_extreme_512k():
     """B=1 H=16 N=524288 d=64 bf16, p=4 L=6 k=1536: the coarsest level (512)
     is below k, so S = 27136 instead of 31232."""
     _run("extreme_512k", [(0, 3)])
+
+
+def test_98k_ablation_p2_L3():
+    """The ablation optimum p=2, L=3, k=1536 on the 98K layer (S=30720)."""
+    _run("ablation_p2_L3_98k", [(0, 9)])
