@@ -177,6 +177,48 @@ def algorithmic_work(name, w, plan):
     return "hbm", BH * table[name], "byte"
 
 
+def attention_block(args, w, layer, o, dod, dq, dk, dv, timed):
+    """The layer with its Q, K, V projections either side (d_model = H d):
+    lh_qkv_forward, the layer forward and backward, lh_qkv_backward -- on the
+    same GPU, inputs x ~ N(0,1) and weights ~ N(0, 1/d_model)."""
+    import torch
+    from long_context_pretraining_amd import inputs
+    from long_context_pretraining_amd import lighthouse as lh
+    Dm = w.H * w.d
+    dev = torch.device("cuda:0")
+    x, wt, _ = inputs.make_proj_inputs(w.B, w.N, Dm, w.H, w.d, w.seed + 2000)
+    x, wt = x.to(dev), wt.to(dev)
+    pdesc = lh.make_proj_desc(w.B, w.N, Dm, w.H, w.d)
+    ws = torch.empty(lh.lh_qkv_plan(pdesc), dtype=torch.uint8, device=dev)
+    q, k, v = (torch.empty_like(dq) for _ in range(3))
+    dx = torch.empty_like(x)
+    dw = torch.empty(wt.shape, dtype=torch.float32, device=dev)
+
+    def fwd():
+        lh.lh_qkv_forward(pdesc, x, wt, q, k, v)
+
+    def bwd():
+        lh.lh_qkv_backward(pdesc, x, wt, dq, dk, dv, dx, dw, ws)
+
+    def whole():
+        fwd()
+        layer.forward(q, k, v, o)
+        layer.backward(dod, dq, dk, dv)
+        bwd()
+
+    n = max(args.steps, 3)
+    f_ms, b_ms, t_ms = timed(fwd, n), timed(bwd, n), timed(whole, n)
+    flop = 2.0 * w.B * w.N * Dm * 3 * w.H * w.d          # one of the three products
+    del ws
+    return {"d_model": Dm, "ms_per_step": round(t_ms, 4),
+            "tokens_per_s": round(w.B * w.N / (t_ms * 1e-3), 1),
+            "qkv_fwd_ms": round(f_ms, 4), "qkv_bwd_ms": round(b_ms, 4),
+            "qkv_fwd_tflops": round(flop / (f_ms * 1e-3) / 1e12, 1),
+            "qkv_bwd_tflops": round(2 * flop / (b_ms * 1e-3) / 1e12, 1),
+            "note": "projections + layer fwd+bwd + projection gradients (dx, dw); "
+                    "TFLOP/s count the GEMM flops only (the backward includes its transposes)"}
+
+
 def cpu_baseline(w, q, k, v, dout, nheads=6):
     """The oracle as it stands on the first `nheads` heads of the workload:
     selection, pyramid, attention, scatter and the whole backward, per head;
@@ -309,6 +351,7 @@ def main():
     del dws, dwsb
     # forward only (selection included), after the timed region
     fwd_ms = timed(lambda: layer.forward(qd, kd, vd, o), args.steps)
+    block = attention_block(args, w, layer, o, dod, dq, dk, dv, timed) if w.dtype == "bf16" else None
 
     if args.calibration_copy:   # a plain copy kernel of known size: reads and writes 1 GiB
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -342,6 +385,7 @@ def main():
         "speedup_fwd_vs_dense": round(dense_fwd_ms / fwd_ms, 3) if dense_fwd_ms else None,
         "kernel_ms": {n: round(x, 4) for n, x in kernel_ms.items()},
         "roofline": roof,
+        "attention_block": block,
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, q, k, v, dout)

@@ -179,6 +179,37 @@ lh_status dense_causal_attn_backward(const lh_desc* desc, const void* q, const v
                                      const void* dout, void* dq, void* dk, void* dv,
                                      void* ws, size_t ws_bytes, void* stream);
 
+/* Q, K, V projections either side of the layer (skill card: the pipeline
+ * starts from the projections of the layer input X; the complexity table
+ * lists them as a GEMM of Theta(N d_model d); the gradient flows back through
+ * gather into W_Q, W_K, W_V).  bf16 only; Dm a multiple of 64; N a multiple
+ * of 64; H*d*3*N*B and B*N*Dm below 2^31.  Products accumulate in f32 on the
+ * matrix cores.
+ *   x:  [B, N, Dm] bf16, the layer input, row-major.
+ *   w:  [3*H*d, Dm] bf16 (out x in): rows 0..Hd-1 project to Q (head h at
+ *       rows h*d..), rows Hd..2Hd-1 to K, rows 2Hd..3Hd-1 to V. */
+typedef struct {
+    int64_t B, N, Dm, H, d;
+} lh_proj_desc;
+
+/* Backward workspace size (transposed copies of W, X and [dQ dK dV], and the
+ * split partials of dW).  Host only. */
+lh_status lh_qkv_plan(const lh_proj_desc* desc, size_t* bwd_ws_bytes);
+
+/* q = x Wq^T, k = x Wk^T, v = x Wv^T, written as [B, H, N, d] bf16 (the
+ * layout lh_pyramid / lh_forward take), one rounding from f32. */
+lh_status lh_qkv_forward(const lh_proj_desc* desc, const void* x, const void* w,
+                         void* q, void* k, void* v, void* stream);
+
+/* Gradients of the projections given dq, dk, dv [B, H, N, d] bf16 (e.g. from
+ * lh_backward): dx = dq Wq + dk Wk + dv Wv  [B, N, Dm] bf16, and
+ * dw = [dq dk dv]^T x summed over all B*N tokens  [3*H*d, Dm] f32 (the
+ * k-split partials are summed in a fixed order: deterministic).
+ * ws: scratch of bwd_ws_bytes from lh_qkv_plan. */
+lh_status lh_qkv_backward(const lh_proj_desc* desc, const void* x, const void* w,
+                          const void* dq, const void* dk, const void* dv,
+                          void* dx, float* dw, void* ws, size_t ws_bytes, void* stream);
+
 /* Static string for a status code. */
 const char* lh_status_string(int status);
 
@@ -193,6 +224,7 @@ enum {
     LH_KERNEL_POOL = 0, LH_KERNEL_SCORE, LH_KERNEL_TOPK, LH_KERNEL_MAP, LH_KERNEL_GATHER,
     LH_KERNEL_ATTN_FWD, LH_KERNEL_SCATTER_FWD, LH_KERNEL_SCATTER_BWD, LH_KERNEL_ATTN_DKDV,
     LH_KERNEL_ATTN_DQ, LH_KERNEL_GATHER_POOL_BWD, LH_KERNEL_TRANSPOSE, LH_KERNEL_DENSE_PREP,
+    LH_KERNEL_QKV_FWD, LH_KERNEL_QKV_BWD,
     LH_KERNEL_COUNT
 };
 lh_status lh_set_probe(int kernel, void* start_event, void* stop_event);

@@ -16,7 +16,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "liblighthouse.so")
 BUILD_DIR = os.path.join(HERE, "_build")
-SOURCES = ["lh_api.hip", "lh_select.hip", "lh_scatter.hip", "lh_attention.hip"]
+SOURCES = ["lh_api.hip", "lh_select.hip", "lh_scatter.hip", "lh_attention.hip", "lh_proj.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

@@ -299,6 +299,62 @@ lh_status dense_causal_attn_backward(const lh_desc* desc, const void* q, const v
     return dev(e);
 }
 
+namespace {
+constexpr int kProjSplits = 4;   // k-splits of the dW product (its k runs over all tokens)
+
+lh_status proj_geom(const lh_proj_desc* d, ProjGeom* g) {
+    if (!d || !g) return LH_E_ARG;
+    if (d->B < 1 || d->N < 1 || d->Dm < 1 || d->H < 1 || d->d < 1) return LH_E_ARG;
+    if (d->Dm % 64 || d->N % 64 || (d->d != 64 && d->d != 128)) return LH_E_UNSUPPORTED;
+    const int64_t Nc = 3 * d->H * d->d, M = d->B * d->N;
+    if (Nc * M >= (int64_t(1) << 31) || M * d->Dm >= (int64_t(1) << 31) || Nc * d->Dm >= (int64_t(1) << 31))
+        return LH_E_UNSUPPORTED;
+    ProjGeom G{};
+    G.B = d->B; G.N = d->N; G.Dm = d->Dm; G.H = d->H; G.d = d->d;
+    G.splits = kProjSplits;
+    size_t off = 0;
+    G.ws_wT = off; off += align_up((size_t)d->Dm * Nc * 2);
+    G.ws_xT = off; off += align_up((size_t)d->Dm * M * 2);
+    G.ws_gT = off; off += align_up((size_t)Nc * M * 2);
+    G.ws_part = off; off += align_up((size_t)G.splits * Nc * d->Dm * 4);
+    G.ws_bytes = off;
+    *g = G;
+    return LH_OK;
+}
+}  // namespace
+
+lh_status lh_qkv_plan(const lh_proj_desc* desc, size_t* bwd_ws_bytes) {
+    ProjGeom g;
+    if (!bwd_ws_bytes) return LH_E_ARG;
+    const lh_status s = proj_geom(desc, &g);
+    if (s == LH_OK) *bwd_ws_bytes = g.ws_bytes;
+    return s;
+}
+
+lh_status lh_qkv_forward(const lh_proj_desc* desc, const void* x, const void* w, void* q, void* k, void* v,
+                         void* stream) {
+    ProjGeom g;
+    const lh_status s = proj_geom(desc, &g);
+    if (s != LH_OK) return s;
+    if (!aligned(x) || !aligned(w) || !aligned(q) || !aligned(k) || !aligned(v)) return LH_E_ARG;
+    hipStream_t st = (hipStream_t)stream;
+    return dev(probed(LH_KERNEL_QKV_FWD, st, [&] { return launch_qkv_forward(g, x, w, q, k, v, st); }));
+}
+
+lh_status lh_qkv_backward(const lh_proj_desc* desc, const void* x, const void* w, const void* dq, const void* dk,
+                          const void* dv, void* dx, float* dw, void* ws, size_t ws_bytes, void* stream) {
+    ProjGeom g;
+    const lh_status s = proj_geom(desc, &g);
+    if (s != LH_OK) return s;
+    if (!aligned(x) || !aligned(w) || !aligned(dq) || !aligned(dk) || !aligned(dv) || !aligned(dx) ||
+        !aligned(dw) || !aligned(ws))
+        return LH_E_ARG;
+    if (ws_bytes < g.ws_bytes) return LH_E_WORKSPACE;
+    hipStream_t st = (hipStream_t)stream;
+    return dev(probed(LH_KERNEL_QKV_BWD, st,
+                      [&] { return launch_qkv_backward(g, x, w, dq, dk, dv, dx, dw, ws, st); }));
+}
+
 lh_status lh_set_probe(int kernel, void* start_event, void* stop_event) {
     if (kernel < -1 || kernel >= LH_KERNEL_COUNT) return LH_E_ARG;
     g_probe_kernel = (start_event && stop_event) ? kernel : -1;

@@ -43,90 +43,6 @@ struct AttnK {
     int nblk;   // row blocks per head
 };
 
-// ---------------------------------------------------------------------------
-// LDS tiles.  A tile is ROWS rows of ROWB bytes, filled straight from global
-// memory by global_load_lds (16 bytes per lane, 1 KB per wave instruction, no
-// staging registers).  16-byte chunk c of row r sits at chunk c ^ f(r) of that
-// row, with f(r) = (r ^ (r >> 3)) & 7 for 128-byte rows and r & 15 for
-// 256-byte rows: lanes reading the same chunk of 8 consecutive rows then hit
-// 8 different 16-byte bank groups of a 128-byte bank window, and 16
-// consecutive rows 16 different groups of a 256-byte window.
-// Row tiles hold 64 rows of a row-major [S][D] array (rows past S repeat row
-// S-1; the masks make them irrelevant).  Column tiles hold D rows of a
-// transposed [D][S_pad] array, 64 keys each, in the slot order the gather and
-// transposes write (see store_transposed): lane half h then finds the 8 keys
-// of its k16 step as one 16-byte run.
-// ---------------------------------------------------------------------------
-typedef __attribute__((address_space(3))) void lds_void;
-
-template <int ROWB>
-__device__ __forceinline__ int swz_key(int row) {
-    static_assert(ROWB == 64 || ROWB == 128 || ROWB == 256, "row tiles of 64, 128 or 256 bytes");
-    if (ROWB == 64) return ((row >> 1) ^ (row >> 3)) & 3;
-    return ROWB == 128 ? ((row ^ (row >> 3)) & 7) : (row & 15);
-}
-template <int ROWB>
-__device__ __forceinline__ int swz(int row, int chunk) { return row * ROWB + ((chunk ^ swz_key<ROWB>(row)) << 4); }
-
-// Loads one tile: chunk (wave * PER + i) * 64 + lane of the tile (byte
-// position pos, tile row r = pos / ROWB) receives global 16-byte chunk
-// (pos % ROWB) / 16 ^ f(r) of row r, found at base + row_off(r).  row_off
-// returns a 32-bit byte offset and base is uniform, so the per-lane address is
-// a single 32-bit value.
-template <int ROWB, int BYTES, int NW, class RowOff>
-__device__ __forceinline__ void stage_tile(unsigned char* tile, const void* base, RowOff row_off) {
-    static_assert(BYTES % (1024 * NW) == 0, "tile must split into 1 KB wave instructions");
-    constexpr int PER_WAVE = BYTES / (1024 * NW);
-    const int lane = threadIdx.x & 63, wave = wave_id();
-#pragma unroll
-    for (int i = 0; i < PER_WAVE; ++i) {
-        const int dst = (wave * PER_WAVE + i) * 1024;
-        const int pos = dst + 16 * lane;
-        const int row = pos / ROWB;
-        const uint32_t chunk = (uint32_t)(((pos % ROWB) >> 4) ^ swz_key<ROWB>(row));
-        const unsigned char* g = reinterpret_cast<const unsigned char*>(base) + (row_off(row) + (chunk << 4));
-        __builtin_amdgcn_global_load_lds(g, (lds_void*)(tile + dst), 16, 0, 0);
-    }
-}
-
-// 8 elements of T starting at element e0 (a multiple of 8) of a tile row.
-template <typename T, int ROWB>
-__device__ __forceinline__ typename Frag<T>::type tile_frag(const unsigned char* tile, int row, int e0);
-template <>
-__device__ __forceinline__ bf16x8 tile_frag<bf16, 64>(const unsigned char* tile, int row, int e0) {
-    return *reinterpret_cast<const bf16x8*>(tile + swz<64>(row, e0 >> 3));
-}
-template <>
-__device__ __forceinline__ bf16x8 tile_frag<bf16, 128>(const unsigned char* tile, int row, int e0) {
-    return *reinterpret_cast<const bf16x8*>(tile + swz<128>(row, e0 >> 3));
-}
-template <>
-__device__ __forceinline__ bf16x8 tile_frag<bf16, 256>(const unsigned char* tile, int row, int e0) {
-    return *reinterpret_cast<const bf16x8*>(tile + swz<256>(row, e0 >> 3));
-}
-template <int ROWB>
-__device__ __forceinline__ floatx8 tile_frag_f32(const unsigned char* tile, int row, int e0) {
-    const floatx4 a = *reinterpret_cast<const floatx4*>(tile + swz<ROWB>(row, e0 >> 2));
-    const floatx4 b = *reinterpret_cast<const floatx4*>(tile + swz<ROWB>(row, (e0 >> 2) + 1));
-    floatx8 r;
-    r.lo = a;
-    r.hi = b;
-    return r;
-}
-template <>
-__device__ __forceinline__ floatx8 tile_frag<float, 128>(const unsigned char* tile, int row, int e0) {
-    return tile_frag_f32<128>(tile, row, e0);
-}
-template <>
-__device__ __forceinline__ floatx8 tile_frag<float, 256>(const unsigned char* tile, int row, int e0) {
-    return tile_frag_f32<256>(tile, row, e0);
-}
-
-__device__ __forceinline__ void wait_tiles_and_sync() {
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-}
-
 __device__ __forceinline__ void block_order(const AttnK& a, bool longest_last_rows, int64_t& bh, int& blk) {
     const int64_t x = blockIdx.x;
     bh = x % a.BH;

@@ -61,3 +61,14 @@ hipError_t launch_attn_dkdv(const AttnArgs& a, int dtype, bool out_f32, const vo
 hipError_t launch_attn_dq(const AttnArgs& a, int dtype, bool out_f32, const void* Q, const void* K, const void* V,
                           const void* KT, const void* dO, const float* nl, const float* nd, void* dQ,
                           hipStream_t st);
+
+// projections (lh_proj.hip)
+struct ProjGeom {
+    int64_t B, N, Dm, H, d;
+    int splits;                                  // k-splits of the dW product
+    size_t ws_wT, ws_xT, ws_gT, ws_part, ws_bytes;   // backward workspace layout (byte offsets)
+};
+hipError_t launch_qkv_forward(const ProjGeom& g, const void* x, const void* w, void* q, void* k, void* v,
+                              hipStream_t st);
+hipError_t launch_qkv_backward(const ProjGeom& g, const void* x, const void* w, const void* dq, const void* dk,
+                               const void* dv, void* dx, float* dw, void* ws, hipStream_t st);

@@ -95,6 +95,18 @@ def make_dout(w: Workload) -> torch.Tensor:
     return _cast(rng.standard_normal((w.B, w.H, w.N, w.d), dtype=np.float32), w.dtype)
 
 
+def make_proj_inputs(B: int, N: int, Dm: int, H: int, d: int, seed: int):
+    """Layer input x ~ N(0,1) [B,N,Dm], projection weights w ~ N(0, 1/Dm)
+    [3Hd, Dm] (the usual fan-in scaling), and upstream gradients dq, dk, dv
+    ~ N(0,1) [B,H,N,d]; all bf16 (round-to-nearest-even), CPU tensors."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    x = rng.standard_normal((B, N, Dm), dtype=np.float32)
+    w = rng.standard_normal((3 * H * d, Dm), dtype=np.float32) * np.float32(1.0 / np.sqrt(Dm))
+    rg = np.random.Generator(np.random.PCG64(seed + 1000))
+    g = [rg.standard_normal((B, H, N, d), dtype=np.float32) for _ in range(3)]
+    return _cast(x, "bf16"), _cast(w, "bf16"), [_cast(a, "bf16") for a in g]
+
+
 def make_random(shape, seed: int, dtype: str, scale: float = 1.0) -> torch.Tensor:
     """Generic N(0, scale^2) tensor for small ad-hoc cases."""
     rng = np.random.Generator(np.random.PCG64(seed))

@@ -42,6 +42,11 @@ class LhPlan(ctypes.Structure):
                 ("fwd_off", ctypes.c_size_t * 8), ("bwd_off", ctypes.c_size_t * 7)]
 
 
+class LhProjDesc(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int64), ("N", ctypes.c_int64), ("Dm", ctypes.c_int64), ("H", ctypes.c_int64),
+                ("d", ctypes.c_int64)]
+
+
 class LighthouseError(RuntimeError):
     def __init__(self, status: int, where: str):
         super().__init__(f"{where}: {status_string(status)} (status {status})")
@@ -60,13 +65,16 @@ _SIGS = {
     "dense_causal_attn": [ctypes.POINTER(LhDesc), _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP],
     "dense_causal_attn_backward": [ctypes.POINTER(LhDesc), _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
                                    _SZ, _VP],
+    "lh_qkv_plan": [ctypes.POINTER(LhProjDesc), ctypes.POINTER(ctypes.c_size_t)],
+    "lh_qkv_forward": [ctypes.POINTER(LhProjDesc), _VP, _VP, _VP, _VP, _VP, _VP],
+    "lh_qkv_backward": [ctypes.POINTER(LhProjDesc), _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP],
     "lh_status_string": [ctypes.c_int],
     "lh_set_probe": [ctypes.c_int, _VP, _VP],
 }
 
 (KERNEL_POOL, KERNEL_SCORE, KERNEL_TOPK, KERNEL_MAP, KERNEL_GATHER, KERNEL_ATTN_FWD, KERNEL_SCATTER_FWD,
  KERNEL_SCATTER_BWD, KERNEL_ATTN_DKDV, KERNEL_ATTN_DQ, KERNEL_GATHER_POOL_BWD, KERNEL_TRANSPOSE,
- KERNEL_DENSE_PREP) = range(13)
+ KERNEL_DENSE_PREP, KERNEL_QKV_FWD, KERNEL_QKV_BWD) = range(15)
 
 
 def header_functions() -> list:
@@ -167,6 +175,26 @@ def dense_causal_attn_backward(desc, q, k, v, lse, fwd_ws, dout, dq, dk, dv, ws,
     _check(load_library().dense_causal_attn_backward(ctypes.byref(desc), _p(q), _p(k), _p(v), _p(lse),
                                                      _p(fwd_ws), _p(dout), _p(dq), _p(dk), _p(dv), _p(ws),
                                                      _nbytes(ws), _stream(stream)), "dense_causal_attn_backward")
+
+
+def make_proj_desc(B, N, Dm, H, d) -> LhProjDesc:
+    return LhProjDesc(B, N, Dm, H, d)
+
+
+def lh_qkv_plan(desc: LhProjDesc) -> int:
+    n = ctypes.c_size_t()
+    _check(load_library().lh_qkv_plan(ctypes.byref(desc), ctypes.byref(n)), "lh_qkv_plan")
+    return n.value
+
+
+def lh_qkv_forward(desc, x, w, q, k, v, stream=None):
+    _check(load_library().lh_qkv_forward(ctypes.byref(desc), _p(x), _p(w), _p(q), _p(k), _p(v), _stream(stream)),
+           "lh_qkv_forward")
+
+
+def lh_qkv_backward(desc, x, w, dq, dk, dv, dx, dw, ws, stream=None):
+    _check(load_library().lh_qkv_backward(ctypes.byref(desc), _p(x), _p(w), _p(dq), _p(dk), _p(dv), _p(dx),
+                                          _p(dw), _p(ws), _nbytes(ws), _stream(stream)), "lh_qkv_backward")
 
 
 # ---------------------------------------------------------------------------

@@ -412,3 +412,42 @@ def dense_forward(q, k, v, dtype, scale=None):
     selection-attention decoupling: switching selection off gives dense)."""
     N = q.shape[0]
     return head_forward(q, k, v, 2, 1, 1, dtype, scale)
+
+
+# ------------------------------------------------------------------ projections
+# [SK] "four-stage pipeline": the layer starts from the Q, K, V projections of
+# its input X; "complexity": the projections are a GEMM of Theta(N d_model d);
+# "gradient flow": the gradient reaches W_Q, W_K, W_V through gather (none
+# through selection).  Reading: one weight matrix w [3 H d, Dm] in the
+# out x in convention, rows Q then K then V, head h of each at rows h d ..
+# (h+1) d - 1 (multi-head attention with H heads of size d for Q, K and V).
+
+def qkv_project(x, w, H, d, dtype):
+    """x [B,N,Dm], w [3Hd, Dm] -> q, k, v [B,H,N,d]: q[b,h,n] = x[b,n] . w[h d + j]
+    for j < d (k and v from the next H d rows), in float64 (a library matrix
+    product), each output rounded once to dtype."""
+    B, N, Dm = x.shape
+    if w.shape != (3 * H * d, Dm):
+        raise ValueError("w must be [3*H*d, Dm]")
+    y = np.asarray(x, dtype=np.float64) @ np.asarray(w, dtype=np.float64).T      # [B, N, 3Hd]
+    y = y.reshape(B, N, 3, H, d).transpose(2, 0, 3, 1, 4)                       # [3, B, H, N, d]
+    return tuple(round_to(y[i], dtype) for i in range(3))
+
+
+def qkv_features(dq, dk, dv):
+    """[B,H,N,d] x 3 -> [B, N, 3Hd] with feature index (which, h, j) as in w's rows."""
+    g = np.stack([np.asarray(a, dtype=np.float64) for a in (dq, dk, dv)])         # [3, B, H, N, d]
+    three, B, H, N, d = g.shape
+    return g.transpose(1, 3, 0, 2, 4).reshape(B, N, 3 * H * d)
+
+
+def qkv_project_backward(x, w, dq, dk, dv, dtype):
+    """Gradients of sum(q dq + k dk + v dv) for q, k, v = qkv_project(x, w):
+    dx [B,N,Dm] = G w (rounded once to dtype) and dw [3Hd, Dm] = G^T x summed
+    over all B N tokens (float64), where G [B,N,3Hd] = qkv_features(dq, dk, dv)."""
+    G = qkv_features(dq, dk, dv)
+    B, N, F = G.shape
+    x64 = np.asarray(x, dtype=np.float64)
+    dx = round_to(G @ np.asarray(w, dtype=np.float64), dtype)
+    dw = G.reshape(B * N, F).T @ x64.reshape(B * N, -1)
+    return dx, dw

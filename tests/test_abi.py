@@ -16,7 +16,8 @@ def test_exports_every_header_function():
     lib = lh.load_library()
     names = lh.header_functions()
     assert set(names) == {"lh_make_plan", "lh_pyramid", "lh_score_topk", "lh_forward", "lh_backward",
-                          "dense_causal_attn", "dense_causal_attn_backward", "lh_status_string", "lh_set_probe"}
+                          "dense_causal_attn", "dense_causal_attn_backward", "lh_status_string", "lh_set_probe",
+                          "lh_qkv_plan", "lh_qkv_forward", "lh_qkv_backward"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -110,6 +111,28 @@ def test_tensor_marshalling_rejects_host_tensors():
 def test_probe_hook_validates_kernel_id():
     lib = lh.load_library()
     assert lib.lh_set_probe(-1, None, None) == lh.LH_OK
-    assert lib.lh_set_probe(13, None, None) == lh.LH_E_ARG
+    assert lib.lh_set_probe(15, None, None) == lh.LH_E_ARG
     assert lib.lh_set_probe(-2, None, None) == lh.LH_E_ARG
     assert lib.lh_set_probe(lh.KERNEL_ATTN_DKDV, None, None) == lh.LH_OK   # null events: off
+
+
+def test_projection_plan_and_argument_checks():
+    """Projection calls: sizes on the host, shape/alignment checks before any launch."""
+    lib = lh.load_library()
+    B, N, Dm, H, d = 2, 128, 128, 2, 64
+    n = lh.lh_qkv_plan(lh.make_proj_desc(B, N, Dm, H, d))
+    Nc, M = 3 * H * d, B * N
+    assert n >= Dm * Nc * 2 + Dm * M * 2 + Nc * M * 2 + 4 * Nc * Dm * 4
+    for bad, status in [((B, 100, Dm, H, d), lh.LH_E_UNSUPPORTED),    # N not a multiple of 64
+                        ((B, N, 96, H, d), lh.LH_E_UNSUPPORTED),      # Dm not a multiple of 64
+                        ((B, N, Dm, H, 96), lh.LH_E_UNSUPPORTED),     # d not built
+                        ((0, N, Dm, H, d), lh.LH_E_ARG)]:
+        with pytest.raises(lh.LighthouseError) as e:
+            lh.lh_qkv_plan(lh.make_proj_desc(*bad))
+        assert e.value.status == status
+    desc = lh.make_proj_desc(B, N, Dm, H, d)
+    fake = 1 << 20   # aligned, never dereferenced: the checks fail before any launch
+    assert lib.lh_qkv_forward(ctypes.byref(desc), None, fake, fake, fake, fake, None) == lh.LH_E_ARG
+    assert lib.lh_qkv_forward(ctypes.byref(desc), fake + 2, fake, fake, fake, fake, None) == lh.LH_E_ARG
+    assert lib.lh_qkv_backward(ctypes.byref(desc), fake, fake, fake, fake, fake, fake, fake, fake, n - 1,
+                               None) == lh.LH_E_WORKSPACE
