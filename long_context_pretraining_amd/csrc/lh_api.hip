@@ -300,7 +300,16 @@ lh_status dense_causal_attn_backward(const lh_desc* desc, const void* q, const v
 }
 
 namespace {
-constexpr int kProjSplits = 4;   // k-splits of the dW product (its k runs over all tokens)
+// The dW product has few 256 x 256 output tiles (3Hd x Dm) and a long k (every
+// token): its k is split so that tiles x splits comes close to one block per CU
+// (256 CUs), at most 16 ways and never below one 64-token k-block per split.
+int proj_splits(int64_t Nc, int64_t Dm, int64_t M) {
+    const int64_t tiles = ((Nc + 255) / 256) * ((Dm + 255) / 256);
+    int64_t s = 256 / tiles;
+    if (s > 16) s = 16;
+    if (s > M / 64) s = M / 64;
+    return s < 1 ? 1 : (int)s;
+}
 
 lh_status proj_geom(const lh_proj_desc* d, ProjGeom* g) {
     if (!d || !g) return LH_E_ARG;
@@ -311,7 +320,7 @@ lh_status proj_geom(const lh_proj_desc* d, ProjGeom* g) {
         return LH_E_UNSUPPORTED;
     ProjGeom G{};
     G.B = d->B; G.N = d->N; G.Dm = d->Dm; G.H = d->H; G.d = d->d;
-    G.splits = kProjSplits;
+    G.splits = proj_splits(Nc, d->Dm, M);
     size_t off = 0;
     G.ws_wT = off; off += align_up((size_t)d->Dm * Nc * 2);
     G.ws_xT = off; off += align_up((size_t)d->Dm * M * 2);

@@ -20,11 +20,18 @@
 
 namespace {
 
-constexpr int kGThreads = 256;                 // 4 waves, each a 64 x 64 block of C
-constexpr int kBM = 128, kBN = 128, kBK = 64;  // C tile, k per stage
-constexpr int kTileBytes = kBM * kBK * 2;      // one operand tile (bf16, 128-byte rows)
-constexpr int kCLd = kBN + 4;                  // f32 row stride of the staged C tile
-constexpr int kGemmLds = (2 * 2 * kTileBytes > kBM * kCLd * 4) ? 2 * 2 * kTileBytes : kBM * kCLd * 4;
+// Block tile 256 x 256 (8 waves, each 128 rows x 64 columns of C), k in
+// stages of 64 double-buffered in LDS: each stage is 32 matrix products per
+// wave, enough to cover the next stage's global-to-LDS load.
+constexpr int kBM = 256, kBN = 256, kBK = 64;
+constexpr int kWM = 2, kWN = 4;                    // waves along m and n
+constexpr int kGWaves = kWM * kWN, kGThreads = 64 * kGWaves;
+constexpr int kTM = kBM / kWM, kTN = kBN / kWN;    // one wave's block of C
+constexpr int kTileBytes = kBM * kBK * 2;          // one operand tile (bf16, 128-byte rows); kBM == kBN
+constexpr int kCRows = 64, kCLd = kBN + 8;         // C leaves through LDS 64 rows at a time; the
+                                                   // pitch puts lane halves (4 rows apart) on disjoint banks
+constexpr int kGemmLds = (2 * 2 * kTileBytes > kCRows * kCLd * 4) ? 2 * 2 * kTileBytes : kCRows * kCLd * 4;
+static_assert(kBM == kBN, "one tile size for both operands");
 
 // Operand with k-contiguous rows: row r of k-block kb at kblock(kb) + r * row_bytes.
 struct RowMajorOp {
@@ -35,31 +42,42 @@ struct RowMajorOp {
         return reinterpret_cast<const unsigned char*>(p + (int64_t)kb * kBK);
     }
 };
-// [dQ dK dV] of one batch b as rows = tokens, k = feature (which, h, dd).
+// [dQ dK dV] of one batch as rows = tokens, k = feature (which, h, dd): k-block
+// kb covers 64 features of one head.  32-bit index math: the source is picked
+// by comparisons, the head and the offset inside it by shifts (d = 64 or 128).
 struct HeadMajorOp {
-    const bf16 *x0, *x1, *x2;
-    int64_t H, N, d, b;
+    const bf16 *x0, *x1, *x2;        // this batch's [H, N, d] slabs
+    int kb_per_src;                   // H * d / 64
+    int head_shift;                   // log2(d / 64)
+    uint32_t head_stride;             // N * d elements
+    uint32_t row_bytes;               // d * 2
     int64_t rows;
     __device__ const unsigned char* kblock(int kb) const {
-        const int64_t f = (int64_t)kb * kBK;
-        const int64_t which = f / (H * d), h = (f / d) % H, dd = f % d;
+        const int which = (kb >= kb_per_src) + (kb >= 2 * kb_per_src);
+        const int r = kb - which * kb_per_src;
+        const uint32_t h = (uint32_t)r >> head_shift, dd = ((uint32_t)r & ((1u << head_shift) - 1)) * 64;
         const bf16* x = which == 0 ? x0 : (which == 1 ? x1 : x2);
-        return reinterpret_cast<const unsigned char*>(x + ((b * H + h) * N) * d + dd);
+        return reinterpret_cast<const unsigned char*>(x + (h * head_stride + dd));
     }
 };
 template <class Op> __device__ __forceinline__ uint32_t op_row_bytes(const Op& o);
 template <> __device__ __forceinline__ uint32_t op_row_bytes(const RowMajorOp& o) { return (uint32_t)(o.ld * 2); }
-template <> __device__ __forceinline__ uint32_t op_row_bytes(const HeadMajorOp& o) { return (uint32_t)(o.d * 2); }
+template <> __device__ __forceinline__ uint32_t op_row_bytes(const HeadMajorOp& o) { return o.row_bytes; }
 
 // Epilogues: where 8 consecutive output columns n .. n+7 of row m go.
-struct QkvOut {                 // rows = tokens b*N + n, columns = features -> q/k/v [B,H,N,d]
+struct QkvOut {                 // rows = tokens b*N + t, columns = features -> q/k/v [B,H,N,d]
     bf16 *x0, *x1, *x2;
-    int64_t H, N, d;
+    int Hd, log2d;                // H * d, log2(d)
+    uint32_t N;
     __device__ bf16* at(int64_t m, int64_t n) const {
-        const int64_t which = n / (H * d), h = (n / d) % H, dd = n % d;
-        const int64_t b = m / N, t = m - b * N;
+        const int nn = (int)n;
+        const int which = (nn >= Hd) + (nn >= 2 * Hd);
+        const uint32_t f = (uint32_t)(nn - which * Hd);               // h * d + dd
+        const uint32_t b = (uint32_t)m / N, t = (uint32_t)m - b * N;
         bf16* x = which == 0 ? x0 : (which == 1 ? x1 : x2);
-        return x + ((b * H + h) * N + t) * d + dd;
+        // element offset ((b*H + h)*N + t)*d + dd < 2^31 (one of q, k, v)
+        const uint32_t d = 1u << log2d, h = f >> log2d, dd = f & (d - 1);
+        return x + (((b * (uint32_t)(Hd >> log2d) + h) * N + t) << log2d) + dd;
     }
 };
 template <typename OutT>
@@ -81,78 +99,134 @@ template <> __device__ __forceinline__ void store8<float>(float* dst, const floa
     *reinterpret_cast<floatx4*>(dst + 4) = floatx4{v[4], v[5], v[6], v[7]};
 }
 
-// C[M x Nc] (+)= A[M x K] B[Nc x K]^T for the k-blocks [kb0, kb1) of this
-// block's split (blockIdx.z); f32 accumulation, one rounding to OutT.
+// C[M x Nc] = A[M x K] B[Nc x K]^T over the k-blocks of this block's split
+// (blockIdx.z); f32 accumulation, one rounding to OutT.  Blocks are numbered
+// so that each XCD (blocks are dealt to the 8 XCDs in turn) works on a
+// contiguous range of C tiles, row tile by row tile: tiles that share rows of
+// A then share that XCD's L2.
 template <class OpA, class OpB, class Epi, typename OutT>
-__global__ __launch_bounds__(kGThreads, 2) void gemm_nt_kernel(OpA A, OpB B, Epi E, int64_t M, int64_t Nc,
-                                                               int nkb, int kb_per_split) {
+__global__ __launch_bounds__(kGThreads, 1) void gemm_nt_kernel(OpA A, OpB B, Epi E, int64_t M, int64_t Nc,
+                                                               int nkb, int kb_per_split, int tiles_n,
+                                                               int tiles) {
     extern __shared__ __align__(16) unsigned char smem[];
     const int lane = threadIdx.x & 63, wave = wave_id();
     const int col = lane & 31, h = lane >> 5;
-    const int wm = wave >> 1, wn = wave & 1;
-    const int64_t m0 = (int64_t)blockIdx.y * kBM, n0 = (int64_t)blockIdx.x * kBN;
+    const int wm = wave / kWN, wn = wave % kWN;
+    const int per_xcd = (tiles + 7) / 8;
+    const int tile = (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8);
+    if (tile >= tiles) return;   // uniform per block
+    const int64_t m0 = (int64_t)(tile / tiles_n) * kBM, n0 = (int64_t)(tile % tiles_n) * kBN;
     const int kb0 = blockIdx.z * kb_per_split;
     const int kb1 = kb0 + kb_per_split < nkb ? kb0 + kb_per_split : nkb;
 
     const uint32_t a_rb = op_row_bytes(A), b_rb = op_row_bytes(B);
     const uint32_t a_last = (uint32_t)(A.rows - 1), b_last = (uint32_t)(B.rows - 1);
     auto stage = [&](int kb, unsigned char* buf) {
-        stage_tile<128, kTileBytes, 4>(buf, A.kblock(kb), [&](int r) {
+        stage_tile<128, kTileBytes, kGWaves>(buf, A.kblock(kb), [&](int r) {
             const uint32_t row = (uint32_t)m0 + r < a_last ? (uint32_t)m0 + r : a_last;
             return row * a_rb;
         });
-        stage_tile<128, kTileBytes, 4>(buf + kTileBytes, B.kblock(kb), [&](int r) {
+        stage_tile<128, kTileBytes, kGWaves>(buf + kTileBytes, B.kblock(kb), [&](int r) {
             const uint32_t row = (uint32_t)n0 + r < b_last ? (uint32_t)n0 + r : b_last;
             return row * b_rb;
         });
     };
 
-    floatx16 acc[2][2];
+    constexpr int FI = kTM / 32, FJ = kTN / 32, NS = kBK / 16;
+    floatx16 acc[FI][FJ];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < FI; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = floatx16{};
+        for (int j = 0; j < FJ; ++j) acc[i][j] = floatx16{};
+
+    // Fragments are double-buffered in registers: the reads for k-substep s+1
+    // are issued before the products of substep s, and those for substep 0 of
+    // the next stage right after the barrier that makes it visible, so the
+    // matrix cores never wait for a fresh LDS read at a stage boundary.
+    bf16x8 fa[2][FI], fb[2][FJ];
+    auto read_frags = [&](const unsigned char* t, int s, bf16x8* a, bf16x8* b) {
+#pragma unroll
+        for (int i = 0; i < FI; ++i) a[i] = tile_frag<bf16, 128>(t, wm * kTM + 32 * i + col, 16 * s + 8 * h);
+#pragma unroll
+        for (int j = 0; j < FJ; ++j) b[j] = tile_frag<bf16, 128>(t + kTileBytes, wn * kTN + 32 * j + col, 16 * s + 8 * h);
+    };
+    auto products = [&](const bf16x8* a, const bf16x8* b) {
+#pragma unroll
+        for (int i = 0; i < FI; ++i)
+#pragma unroll
+            for (int j = 0; j < FJ; ++j) mma_k16(acc[i][j], a[i], b[j]);
+    };
+    auto buffer = [&](int kb) { return smem + ((kb - kb0) & 1) * 2 * kTileBytes; };
+    // Scheduling pattern for one substep: one product, then the FI+FJ reads
+    // for the next substep, then the remaining products.  With global-to-LDS
+    // loads in flight the compiler can only wait for every outstanding LDS
+    // read; that wait now falls before the first product, when the reads it
+    // covers were issued a whole substep earlier.
+    auto interleave = [] {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);             // matrix product
+        __builtin_amdgcn_sched_group_barrier(0x100, FI + FJ, 0);       // LDS reads
+        __builtin_amdgcn_sched_group_barrier(0x008, FI * FJ - 1, 0);   // matrix products
+    };
+    static_assert(NS % 2 == 0, "substeps alternate between the two fragment sets");
+
+    // One k-stage.  On entry substep 0's fragments of stage kb are in flight
+    // and stage kb+1 is being loaded into the other buffer.  LOAD2: stage kb+2
+    // exists; NEXT: stage kb+1 exists.
+    auto iteration = [&]<bool LOAD2, bool NEXT>(int kb) {
+        const unsigned char* t = buffer(kb);
+#pragma unroll
+        for (int s = 0; s + 1 < NS; ++s) {
+            read_frags(t, s + 1, fa[(s + 1) & 1], fb[(s + 1) & 1]);
+            products(fa[s & 1], fb[s & 1]);
+            interleave();
+        }
+        // stage kb+1 has landed and every wave holds its last fragments of stage kb
+        wait_tiles_and_sync();
+        if constexpr (LOAD2) stage(kb + 2, buffer(kb));
+        if constexpr (NEXT) read_frags(buffer(kb + 1), 0, fa[0], fb[0]);
+        products(fa[(NS - 1) & 1], fb[(NS - 1) & 1]);
+        if constexpr (NEXT) interleave();
+    };
 
     if (kb0 < kb1) stage(kb0, smem);
     wait_tiles_and_sync();
-    for (int kb = kb0; kb < kb1; ++kb) {
-        const int buf = (kb - kb0) & 1;
-        if (kb + 1 < kb1) stage(kb + 1, smem + (buf ^ 1) * 2 * kTileBytes);
-        const unsigned char* ta = smem + buf * 2 * kTileBytes;
-        const unsigned char* tb = ta + kTileBytes;
-#pragma unroll
-        for (int s = 0; s < kBK / 16; ++s) {
-            bf16x8 af[2], bfr[2];
-#pragma unroll
-            for (int i = 0; i < 2; ++i) af[i] = tile_frag<bf16, 128>(ta, wm * 64 + 32 * i + col, 16 * s + 8 * h);
-#pragma unroll
-            for (int j = 0; j < 2; ++j) bfr[j] = tile_frag<bf16, 128>(tb, wn * 64 + 32 * j + col, 16 * s + 8 * h);
-#pragma unroll
-            for (int i = 0; i < 2; ++i)
-#pragma unroll
-                for (int j = 0; j < 2; ++j) mma_k16(acc[i][j], af[i], bfr[j]);
-        }
-        wait_tiles_and_sync();
-    }
+    if (kb0 + 1 < kb1) stage(kb0 + 1, buffer(kb0 + 1));
+    if (kb0 < kb1) read_frags(smem, 0, fa[0], fb[0]);
+    int kb = kb0;
+    for (; kb + 2 < kb1; ++kb) iteration.template operator()<true, true>(kb);
+    if (kb + 1 < kb1) iteration.template operator()<false, true>(kb++);
+    if (kb < kb1) iteration.template operator()<false, false>(kb);
 
-    // C tile through LDS, then 8-column chunks to global memory
+    // C leaves through LDS, kCRows rows at a time, as 8-column chunks
     float* ct = reinterpret_cast<float*>(smem);
+    static_assert(kTM % kCRows == 0 && kCRows % 32 == 0, "whole row tiles per pass");
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int pass = 0; pass < kBM / kCRows; ++pass) {
+        const int r0 = pass * kCRows;
+        if (wm * kTM <= r0 && r0 < (wm + 1) * kTM) {   // this wave's rows
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+            for (int i = 0; i < FI; ++i) {
+                const int row_base = wm * kTM + 32 * i - r0;
+                if (row_base < 0 || row_base >= kCRows) continue;
 #pragma unroll
-            for (int r = 0; r < 16; ++r)
-                ct[(wm * 64 + 32 * i + c_row(r, h)) * kCLd + wn * 64 + 32 * j + col] = acc[i][j][r];
-    __syncthreads();
-    for (int task = threadIdx.x; task < kBM * (kBN / 8); task += kGThreads) {
-        const int r = task / (kBN / 8), c = task - r * (kBN / 8);
-        const int64_t m = m0 + r, n = n0 + 8 * c;
-        if (m >= M || n >= Nc) continue;
-        float v[8];
+                for (int j = 0; j < FJ; ++j)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = ct[r * kCLd + 8 * c + e];
-        store8<OutT>(E.at(m, n), v);
+                    for (int r = 0; r < 16; ++r)
+                        ct[(row_base + c_row(r, h)) * kCLd + wn * kTN + 32 * j + col] = acc[i][j][r];
+            }
+        }
+        __syncthreads();
+        for (int task = threadIdx.x; task < kCRows * (kBN / 8); task += kGThreads) {
+            const int r = task / (kBN / 8), c = task - r * (kBN / 8);
+            const int64_t m = m0 + r0 + r, n = n0 + 8 * c;
+            if (m < M && n < Nc) {
+                float v[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) v[e] = ct[r * kCLd + 8 * c + e];
+                store8<OutT>(E.at(m, n), v);
+            }
+        }
+        __syncthreads();
     }
 }
 
@@ -206,12 +280,13 @@ hipError_t gemm_nt(const OpA& A, const OpB& B, const Epi& E, int64_t M, int64_t 
                    hipStream_t st) {
     const int nkb = (int)(K / kBK);
     const int per = (nkb + splits - 1) / splits;
+    const int tiles_n = (int)((Nc + kBN - 1) / kBN), tiles = tiles_n * (int)((M + kBM - 1) / kBM);
     auto kern = gemm_nt_kernel<OpA, OpB, Epi, OutT>;
     static const hipError_t attr =
         hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, kGemmLds);
     (void)attr;
-    dim3 grid((unsigned)((Nc + kBN - 1) / kBN), (unsigned)((M + kBM - 1) / kBM), (unsigned)splits);
-    kern<<<grid, kGThreads, kGemmLds, st>>>(A, B, E, M, Nc, nkb, per);
+    dim3 grid((unsigned)((tiles + 7) / 8 * 8), 1, (unsigned)splits);
+    kern<<<grid, kGThreads, kGemmLds, st>>>(A, B, E, M, Nc, nkb, per, tiles_n, tiles);
     return hipGetLastError();
 }
 
@@ -228,7 +303,7 @@ hipError_t launch_qkv_forward(const ProjGeom& g, const void* x, const void* w, v
     const int64_t M = g.B * g.N, Nc = 3 * g.H * g.d;
     RowMajorOp A{(const bf16*)x, g.Dm, M};
     RowMajorOp B{(const bf16*)w, g.Dm, Nc};
-    QkvOut E{(bf16*)q, (bf16*)k, (bf16*)v, g.H, g.N, g.d};
+    QkvOut E{(bf16*)q, (bf16*)k, (bf16*)v, (int)(g.H * g.d), g.d == 64 ? 6 : 7, (uint32_t)g.N};
     return gemm_nt<RowMajorOp, RowMajorOp, QkvOut, bf16>(A, B, E, M, Nc, g.Dm, 1, st);
 }
 
@@ -243,7 +318,9 @@ hipError_t launch_qkv_backward(const ProjGeom& g, const void* x, const void* w, 
     hipError_t e = transpose(TransposeSlabs{(const bf16*)w, nullptr, nullptr, wT, Nc, Dm, Dm, Nc, 1, 0, 0, 0}, 1, st);
     // dX = [dQ dK dV] W, per batch (rows: the batch's tokens)
     for (int64_t b = 0; b < g.B && e == hipSuccess; ++b) {
-        HeadMajorOp A{(const bf16*)dq, (const bf16*)dk, (const bf16*)dv, g.H, g.N, g.d, b, g.N};
+        const int64_t boff = b * g.H * g.N * g.d;
+        HeadMajorOp A{(const bf16*)dq + boff, (const bf16*)dk + boff, (const bf16*)dv + boff,
+                      (int)(g.H * g.d / 64), g.d == 64 ? 0 : 1, (uint32_t)(g.N * g.d), (uint32_t)(g.d * 2), g.N};
         RowMajorOp B{wT, Nc, Dm};
         RowMajorOut<bf16> E{(bf16*)dx + b * g.N * Dm, Dm, 0};
         e = gemm_nt<HeadMajorOp, RowMajorOp, RowMajorOut<bf16>, bf16>(A, B, E, g.N, Dm, Nc, 1, st);

@@ -2,8 +2,10 @@
 lh_qkv_backward, through the C ABI) against the oracle on seeded inputs.
 bf16 outputs (q, k, v, dx) within 2e-2*max(1,|ref|) element-wise; dw (f32,
 summed over every token) within 1e-4 of its largest magnitude.  Shapes span
-several 128 x 128 tiles, ragged row and column tiles, d = 64 and 128, and the
-headline layer (B=1 N=98304 Dm=1024 H=16 d=64) on sampled rows and columns."""
+single partial 256 x 256 tiles, several tiles with ragged row and column tails,
+a batch boundary inside a row tile, dW k-splits of which some are empty, d = 64
+and 128, and the headline layer (B=1 N=98304 Dm=1024 H=16 d=64) on sampled
+rows and columns."""
 import numpy as np
 import pytest
 import torch
@@ -56,6 +58,9 @@ def _compare_full(data, out, H, d, tag):
     (1, 192, 192, 3, 64),    # ragged row and column tiles (192 = 1.5 tiles), 3 k-blocks
     (2, 320, 256, 1, 128),   # d = 128: a head spans two k-blocks
     (1, 64, 64, 1, 64),      # a single partial tile everywhere
+    (1, 576, 320, 2, 64),    # 2.25 x 1.5 tiles forward, 1.25-tile dX columns, 9 one-block dW splits
+    (2, 1088, 512, 4, 64),   # batch boundary inside a row tile; 16 dW splits of 3 k-blocks, the last ones empty
+    (1, 640, 384, 2, 128),   # d = 128 over several tiles
 ])
 def test_projection_parity_small(B, N, Dm, H, d):
     tag = f"proj B{B} N{N} Dm{Dm} H{H} d{d}"
