@@ -84,8 +84,16 @@ def stored_traffic(kernel):
     return int(fields["hbm_bytes_per_launch"])
 
 
+# the three instantiations of the projection GEMM, told apart by their operand / epilogue types
+GEMM_ROLES = (("QkvOut", "qkv_fwd"), ("HeadMajorOp", "qkv_dx"), ("RowMajorOut<float>", "qkv_dw"),
+              ("RowMajorOutIf", "qkv_dw"))
+
+
 def short_kernel_name(name):
     import re
+    if "gemm_nt_kernel" in name:
+        role = next((r for key, r in GEMM_ROLES if key in name), "?")
+        return f"gemm_nt_kernel[{role}]"
     m = re.search(r"_GLOBAL__N_1(\d+)", name)   # mangled: <length><identifier>
     if m:
         return name[m.end():m.end() + int(m.group(1))]
