@@ -295,8 +295,8 @@ def attention_backward(Qt, Kt, Vt, Ot, dOt, lse, scale: float, row_block: int = 
         r1 = min(S, r0 + row_block)
         Z = scale * (Qt[r0:r1] @ Kt[:r1].T)
         rows = np.arange(r0, r1)[:, None]
+        Z[np.arange(r1)[None, :] > rows] = -np.inf    # causal mask before exponentiating
         P = np.exp(Z - lse[r0:r1, None])
-        P[np.arange(r1)[None, :] > rows] = 0.0
         dP = dOt[r0:r1] @ Vt[:r1].T
         dS = P * (dP - D[r0:r1, None])
         dQ[r0:r1] = scale * (dS @ Kt[:r1])
