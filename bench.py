@@ -48,11 +48,25 @@ def parse():
     return ap.parse_args()
 
 
-# Files whose content determines the attention kernels' code: a stored HBM
-# traffic figure is reported only while they are unchanged.
-ATTN_SOURCES = ["long_context_pretraining_amd/csrc/lh_attention.hip", "long_context_pretraining_amd/csrc/lh_device.h",
-                "long_context_pretraining_amd/csrc/lh_internal.h"]
-TRAFFIC_PROFILE = "profiles/{kernel}_98k_k1536_hbm_traffic.md"
+# Files whose content determines each group of kernels: a stored HBM traffic
+# figure is reported only while its group's files are unchanged.
+_CSRC = "long_context_pretraining_amd/csrc/"
+SOURCE_GROUPS = {
+    "attn": [_CSRC + "lh_attention.hip", _CSRC + "lh_device.h", _CSRC + "lh_internal.h"],
+    "select": [_CSRC + "lh_select.hip", _CSRC + "lh_device.h", _CSRC + "lh_internal.h"],
+    "scatter": [_CSRC + "lh_scatter.hip", _CSRC + "lh_device.h", _CSRC + "lh_internal.h"],
+    "proj": [_CSRC + "lh_proj.hip", _CSRC + "lh_device.h", _CSRC + "lh_internal.h"],
+}
+ATTN_SOURCES = SOURCE_GROUPS["attn"]
+# bench name -> kernel symbol as the profiles name it, and its source group
+KERNEL_SYMBOLS = {
+    "pool": ("pool_kernel", "select"), "score": ("score_kernel", "select"), "topk": ("topk_kernel", "select"),
+    "map": ("map_kernel", "select"), "gather": ("gather_kernel", "scatter"),
+    "attn_fwd": ("attn_fwd_kernel", "attn"), "scatter_fwd": ("scatter_fwd_kernel", "scatter"),
+    "scatter_bwd": ("scatter_bwd_kernel", "scatter"), "attn_dkdv": ("attn_dkdv_kernel", "attn"),
+    "attn_dq": ("attn_dq_kernel", "attn"), "gather_pool_bwd": ("gpool_bwd_kernel", "scatter"),
+}
+TRAFFIC_PROFILE = "profiles/lighthouse_98k_k1536_hbm_traffic.md"
 
 
 def sources_sha256(paths):
@@ -65,13 +79,26 @@ def sources_sha256(paths):
     return h.hexdigest()
 
 
-def stored_traffic(kernel):
-    """HBM bytes per launch of `kernel` from its committed counter summary
-    (FETCH_SIZE + WRITE_SIZE, each scaled by a plain copy of known size), or
-    None when there is none or the kernel sources changed since."""
+def symbol_group(symbol):
+    for sym, group in KERNEL_SYMBOLS.values():
+        if sym == symbol:
+            return group
+    if symbol.startswith("gemm_nt_kernel") or symbol in ("transpose_slabs_kernel", "reduce_splits_kernel"):
+        return "proj"
+    return None
+
+
+def stored_traffic(kernel, workload="llama530m_98k_k1536"):
+    """HBM bytes per launch of bench kernel `kernel` from the committed counter
+    summary of the headline workload (FETCH_SIZE + WRITE_SIZE, each scaled by
+    a plain copy of known size), or None when there is none, the workload is
+    another one, or the kernel's sources changed since."""
+    if workload != "llama530m_98k_k1536" or kernel not in KERNEL_SYMBOLS:
+        return None
+    symbol, group = KERNEL_SYMBOLS[kernel]
     root = os.path.dirname(os.path.abspath(__file__))
-    path = os.path.join(root, TRAFFIC_PROFILE.format(kernel=kernel))
-    if not os.path.exists(path) or not kernel.startswith("attn"):
+    path = os.path.join(root, TRAFFIC_PROFILE)
+    if not os.path.exists(path):
         return None
     fields = {}
     with open(path) as f:
@@ -79,9 +106,10 @@ def stored_traffic(kernel):
             if ":" in line and line.startswith("- "):
                 key, val = line[2:].split(":", 1)
                 fields[key.strip()] = val.strip().strip("`")
-    if fields.get("sources_sha256") != sources_sha256(ATTN_SOURCES):
+    if fields.get(f"sources_sha256.{group}") != sources_sha256(SOURCE_GROUPS[group]):
         return None
-    return int(fields["hbm_bytes_per_launch"])
+    val = fields.get(f"hbm_bytes_per_launch.{symbol}")
+    return int(val) if val is not None else None
 
 
 # the three instantiations of the projection GEMM, told apart by their operand / epilogue types
@@ -107,12 +135,14 @@ def pmc_summary(dirs):
     counter averages per kernel of --pmc runs."""
     import csv
     import glob
+    trace_avg = {}
     for d in dirs:
         for path in glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True):
             print("| kernel | calls | total ms | avg us | min us | max us |")
             print("|---|---:|---:|---:|---:|---:|")
             with open(path) as f:
                 for r in csv.DictReader(f):
+                    trace_avg.setdefault(short_kernel_name(r["Name"]), round(float(r["AverageNs"]) / 1e3, 1))
                     print(f"| {short_kernel_name(r['Name'])} | {r['Calls']} | {int(r['TotalDurationNs']) / 1e6:.3f} | "
                           f"{float(r['AverageNs']) / 1e3:.1f} | {int(r['MinNs']) / 1e3:.1f} | {int(r['MaxNs']) / 1e3:.1f} |")
             print()
@@ -135,6 +165,39 @@ def pmc_summary(dirs):
         vals = [f"{agg[(k, c)] / cnt[(k, c)]:.1f}" if (k, c) in agg else "" for c in counters]
         n = max(cnt.get((k, c), 0) for c in counters)
         print(f"| {k} | " + " | ".join(vals) + f" | {n} |")
+    # with both byte counters and the 1 GiB calibration copy: scaled HBM bytes per launch,
+    # the rate over the kernel-trace average (when a trace directory was given) and the
+    # machine-read lines stored_traffic() takes
+    copy = "__amd_rocclr_copyBuffer"
+    if not all((copy, c) in agg for c in ("FETCH_SIZE", "WRITE_SIZE")):
+        return
+    gib_kib = float(1 << 20)
+    f_scale = gib_kib / (agg[(copy, "FETCH_SIZE")] / cnt[(copy, "FETCH_SIZE")])
+    w_scale = gib_kib / (agg[(copy, "WRITE_SIZE")] / cnt[(copy, "WRITE_SIZE")])
+    print()
+    print(f"Calibration: the copy reads and writes {gib_kib:.0f} KiB; fetched bytes = FETCH_SIZE x "
+          f"{f_scale:.5f} x 1024, written bytes = WRITE_SIZE x {w_scale:.5f} x 1024.")
+    print()
+    print("| kernel | HBM MB / launch | avg us | GB/s | of 8000 GB/s |")
+    print("|---|---:|---:|---:|---:|")
+    scaled = {}
+    for k in kernels:
+        if k == copy or (k, "FETCH_SIZE") not in agg or (k, "WRITE_SIZE") not in agg:
+            continue
+        b = (agg[(k, "FETCH_SIZE")] / cnt[(k, "FETCH_SIZE")] * f_scale +
+             agg[(k, "WRITE_SIZE")] / cnt[(k, "WRITE_SIZE")] * w_scale) * 1024
+        scaled[k] = b
+        us = trace_avg.get(k)
+        rate = f"{b / us / 1e3:.0f} | {b / us / 1e3 / HBM_PEAK_GBS * 100:.1f}%" if us else " | "
+        print(f"| {k} | {b / 1e6:.1f} | {us if us else '':} | {rate} |")
+    print()
+    print("Machine-read by bench.py (a group's figures are dropped once its sources change):")
+    print()
+    for k, b in scaled.items():
+        if symbol_group(k):
+            print(f"- hbm_bytes_per_launch.{k}: `{int(b)}`")
+    for g in sorted({symbol_group(k) for k in scaled} - {None}):
+        print(f"- sources_sha256.{g}: `{sources_sha256(SOURCE_GROUPS[g])}`")
 
 
 class HipEvents:
@@ -182,7 +245,8 @@ def algorithmic_work(name, w, plan):
         "topk": Mu * 4,
         "map": plan.M_total * 4 + S * 4,
     }
-    return "hbm", BH * table[name], "byte"
+    # top-K and the map are one pass over a few MB each: bound by latency, not by bytes
+    return ("latency" if name in ("topk", "map") else "hbm"), BH * table[name], "byte"
 
 
 def attention_block(args, w, layer, o, dod, dq, dk, dv, timed):
@@ -324,13 +388,31 @@ def main():
         peak = MFMA_BF16_PEAK_TFS if w.dtype == "bf16" else MFMA_F32_PEAK_TFS
         achieved = work / (dom_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
-                "frac": round(achieved / peak, 4), "traffic": stored_traffic(dominant), "kernel": dominant,
+                "frac": round(achieved / peak, 4), "traffic": stored_traffic(dominant, w.name), "kernel": dominant,
                 "kernel_ms": round(dom_ms, 4), "work_per_launch": work}
     else:
         achieved = work / (dom_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": stored_traffic(dominant), "kernel": dominant,
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": stored_traffic(dominant, w.name), "kernel": dominant,
                 "kernel_ms": round(dom_ms, 4), "work_per_launch": work}
+
+    # every kernel of the step: its algorithmic rate against its roof and, where a counter
+    # summary of this build exists, the HBM bytes it actually moves
+    stages = {}
+    for name, ms in kernel_ms.items():
+        b, wk, _ = algorithmic_work(name, w, plan)
+        st = {"bound": b, "ms": round(ms, 4)}
+        if b == "latency":
+            st.update(alg_gbs=round(wk / (ms * 1e-3) / 1e9, 1))
+        elif b == "mfma":
+            pk = MFMA_BF16_PEAK_TFS if w.dtype == "bf16" else MFMA_F32_PEAK_TFS
+            st.update(alg_tflops=round(wk / (ms * 1e-3) / 1e12, 1), alg_frac=round(wk / (ms * 1e-3) / 1e12 / pk, 3))
+        else:
+            st.update(alg_gbs=round(wk / (ms * 1e-3) / 1e9, 1), alg_frac=round(wk / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 3))
+        hb = stored_traffic(name, w.name)
+        if hb is not None:
+            st.update(hbm_gbs=round(hb / (ms * 1e-3) / 1e9, 1), hbm_frac=round(hb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 3))
+        stages[name] = st
 
     # dense causal attention baseline on the same GPU and inputs
     ddesc = lh.make_desc(w.B, w.H, w.N, w.d, w.p, 1, 1, dt)
@@ -393,6 +475,7 @@ def main():
         "speedup_fwd_vs_dense": round(dense_fwd_ms / fwd_ms, 3) if dense_fwd_ms else None,
         "kernel_ms": {n: round(x, 4) for n, x in kernel_ms.items()},
         "roofline": roof,
+        "stages": stages,
         "attention_block": block,
     }
     if not args.no_cpu_baseline:
