@@ -94,14 +94,17 @@ typedef struct {
      *   FWD_QG, FWD_KG, FWD_VG  gathered Q~, K~, V~   [B,H,S,d] dtype
      *   FWD_QT, FWD_KT, FWD_VT  the same, transposed   [B,H,d,S_pad] dtype (zero past S;
      *                           within each aligned group of 16 slots the order is
-     *                           0-3, 8-11, 4-7, 12-15)
+     *                           0-3, 8-11, 4-7, 12-15) -- f32 only; for bf16 these
+     *                           arrays have size 0 (the kernels read Q~, K~, V~
+     *                           transposed out of LDS)
      *   FWD_O                   sub-sequence output O~ [B,H,S,d] f32 (an
      *                           intermediate: kept unrounded for the scatter and
      *                           for D = rowsum(dO~ * O~) in the backward)
      *   FWD_LSE                 row log-sum-exp (natural log) [B,H,S] f32 */
     size_t fwd_off[8];
     /* Inside the backward workspace:
-     *   BWD_DO, BWD_DOT  dO~ [B,H,S,d] and transposed [B,H,d,S_pad] (same slot order), dtype
+     *   BWD_DO, BWD_DOT  dO~ [B,H,S,d] and transposed [B,H,d,S_pad] (same slot order), dtype;
+     *                    the transposed copy only for f32 (size 0 for bf16)
      *   BWD_NEG_D        -rowsum(dO~ * O~) [B,H,S] f32
      *   BWD_DQ, BWD_DK, BWD_DV  dQ~, dK~, dV~ [B,H,S,d] f32
      *   BWD_NEG_LSE      -(row log-sum-exp) / scale [B,H,S] f32: the offset of

@@ -13,6 +13,12 @@ constexpr size_t kAlign = 256;
 inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 inline int64_t round64(int64_t x) { return (x + 63) / 64 * 64; }
 inline size_t esize(int dtype) { return dtype == LH_BF16 ? 2 : 4; }
+// One transposed [B,H,d,N_pad] array of the dense path (f32 only: the bf16
+// attention kernels read row-major tiles across their rows), rounded for alignment.
+inline size_t dense_transposed_bytes(const lh_desc* d) {
+    if (d->dtype != LH_F32) return 0;
+    return align_up((size_t)d->B * d->H * d->d * round64(d->N) * esize(d->dtype));
+}
 
 bool aligned(const void* p) { return p && ((uintptr_t)p % 16) == 0; }
 
@@ -58,7 +64,8 @@ lh_status plan_impl(const lh_desc* d, lh_plan* out, LhGeom* g) {
     const int64_t BH = d->B * d->H, Mu = P.M_total - d->N;
     const size_t e = esize(d->dtype);
     const size_t row = (size_t)BH * P.S * d->d * e;          // [BH,S,d] dtype
-    const size_t colT = (size_t)BH * d->d * P.S_pad * e;     // [BH,d,S_pad] dtype
+    // [BH,d,S_pad] dtype: transposed copies, taken by the f32 attention kernels only
+    const size_t colT = d->dtype == LH_F32 ? (size_t)BH * d->d * P.S_pad * e : 0;
     const size_t rowf = (size_t)BH * P.S * d->d * 4;         // [BH,S,d] f32
     const size_t vec = (size_t)BH * P.S * 4;                 // [BH,S] f32
 
@@ -72,10 +79,9 @@ lh_status plan_impl(const lh_desc* d, lh_plan* out, LhGeom* g) {
     const size_t bwd_sizes[7] = {row, colT, vec, rowf, rowf, rowf, vec};
     for (int i = 0; i < 7; ++i) { P.bwd_off[i] = o; o += align_up(bwd_sizes[i]); }
     P.bwd_ws_bytes = o;
-    const int64_t N_pad = round64(d->N);
-    const size_t dT = (size_t)BH * d->d * N_pad * e;
-    P.dense_fwd_ws_bytes = align_up(dT) + align_up((size_t)BH * d->N * d->d * 4);
-    P.dense_bwd_ws_bytes = 3 * align_up(dT) + 2 * align_up((size_t)BH * d->N * 4);
+    const size_t dT = dense_transposed_bytes(d);
+    P.dense_fwd_ws_bytes = dT + align_up((size_t)BH * d->N * d->d * 4);
+    P.dense_bwd_ws_bytes = 3 * dT + 2 * align_up((size_t)BH * d->N * 4);
 
     *out = P;
     if (g) {
@@ -177,7 +183,14 @@ lh_status lh_forward(const lh_desc* desc, const void* q, const void* k, const vo
     if (fwd_ws_bytes < P.fwd_ws_bytes) return LH_E_WORKSPACE;
     hipStream_t st = (hipStream_t)stream;
     void* rows[3] = {at(fwd_ws, P.fwd_off[LH_FWD_QG]), at(fwd_ws, P.fwd_off[LH_FWD_KG]), at(fwd_ws, P.fwd_off[LH_FWD_VG])};
-    void* cols[3] = {at(fwd_ws, P.fwd_off[LH_FWD_QT]), at(fwd_ws, P.fwd_off[LH_FWD_KT]), at(fwd_ws, P.fwd_off[LH_FWD_VT])};
+    // transposed copies only for the f32 attention kernels (bf16 reads the row-major rows transposed in LDS)
+    const bool f32 = desc->dtype == LH_F32;
+    void* cols[3] = {nullptr, nullptr, nullptr};
+    if (f32) {
+        cols[0] = at(fwd_ws, P.fwd_off[LH_FWD_QT]);
+        cols[1] = at(fwd_ws, P.fwd_off[LH_FWD_KT]);
+        cols[2] = at(fwd_ws, P.fwd_off[LH_FWD_VT]);
+    }
     float* og = (float*)at(fwd_ws, P.fwd_off[LH_FWD_O]);
     float* lse = (float*)at(fwd_ws, P.fwd_off[LH_FWD_LSE]);
     hipError_t e = probed(LH_KERNEL_GATHER, st,
@@ -185,7 +198,7 @@ lh_status lh_forward(const lh_desc* desc, const void* q, const void* k, const vo
     if (e == hipSuccess) {
         AttnArgs a{g.BH, g.S, g.S_pad, g.d, softmax_scale(desc)};
         e = probed(LH_KERNEL_ATTN_FWD, st, [&] {
-            return launch_attn_fwd(a, desc->dtype, rows[0], rows[1], cols[2], og, nullptr, lse, st);
+            return launch_attn_fwd(a, desc->dtype, rows[0], rows[1], f32 ? cols[2] : rows[2], og, nullptr, lse, st);
         });
     }
     if (e == hipSuccess)
@@ -207,8 +220,9 @@ lh_status lh_backward(const lh_desc* desc, const int32_t* gidx, const int32_t* g
     hipStream_t st = (hipStream_t)stream;
     const float* og = (const float*)at(fwd_ws, P.fwd_off[LH_FWD_O]);
     const float* lse = (const float*)at(fwd_ws, P.fwd_off[LH_FWD_LSE]);
+    const bool f32 = desc->dtype == LH_F32;   // only the f32 kernels take transposed copies
     void* dog = at(bwd_ws, P.bwd_off[LH_BWD_DO]);
-    void* dogT = at(bwd_ws, P.bwd_off[LH_BWD_DOT]);
+    void* dogT = f32 ? at(bwd_ws, P.bwd_off[LH_BWD_DOT]) : nullptr;
     float* nd = (float*)at(bwd_ws, P.bwd_off[LH_BWD_NEG_D]);
     float* nl = (float*)at(bwd_ws, P.bwd_off[LH_BWD_NEG_LSE]);
     float* dxg[3] = {(float*)at(bwd_ws, P.bwd_off[LH_BWD_DQ]), (float*)at(bwd_ws, P.bwd_off[LH_BWD_DK]),
@@ -223,13 +237,13 @@ lh_status lh_backward(const lh_desc* desc, const int32_t* gidx, const int32_t* g
     AttnArgs a{g.BH, g.S, g.S_pad, g.d, softmax_scale(desc)};
     if (e == hipSuccess)
         e = probed(LH_KERNEL_ATTN_DKDV, st, [&] {
-            return launch_attn_dkdv(a, desc->dtype, true, Qg, Kg, Vg, at(fwd_ws, P.fwd_off[LH_FWD_QT]), dog, dogT,
-                                    nl, nd, dxg[1], dxg[2], st);
+            return launch_attn_dkdv(a, desc->dtype, true, Qg, Kg, Vg, f32 ? at(fwd_ws, P.fwd_off[LH_FWD_QT]) : nullptr,
+                                    dog, dogT, nl, nd, dxg[1], dxg[2], st);
         });
     if (e == hipSuccess)
         e = probed(LH_KERNEL_ATTN_DQ, st, [&] {
-            return launch_attn_dq(a, desc->dtype, true, Qg, Kg, Vg, at(fwd_ws, P.fwd_off[LH_FWD_KT]), dog, nl, nd,
-                                  dxg[0], st);
+            return launch_attn_dq(a, desc->dtype, true, Qg, Kg, Vg, f32 ? at(fwd_ws, P.fwd_off[LH_FWD_KT]) : nullptr,
+                                  dog, nl, nd, dxg[0], st);
         });
     if (e == hipSuccess) {
         const float* cg[3] = {dxg[0], dxg[1], dxg[2]};
@@ -249,14 +263,16 @@ lh_status dense_causal_attn(const lh_desc* desc, const void* q, const void* k, c
     if (ws_bytes < P.dense_fwd_ws_bytes) return LH_E_WORKSPACE;
     hipStream_t st = (hipStream_t)stream;
     const int64_t BH = desc->B * desc->H, N = desc->N, N_pad = round64(N);
-    const size_t dT = align_up((size_t)BH * desc->d * N_pad * esize(desc->dtype));
+    const size_t dT = dense_transposed_bytes(desc);
     float* o32 = (float*)at(ws, dT);
-    hipError_t e = probed(LH_KERNEL_TRANSPOSE, st,
-                          [&] { return launch_transpose(desc->dtype, BH, N, N_pad, desc->d, v, ws, st); });
+    const bool f32 = desc->dtype == LH_F32;   // only the f32 kernels take V^T
+    hipError_t e = f32 ? probed(LH_KERNEL_TRANSPOSE, st,
+                                [&] { return launch_transpose(desc->dtype, BH, N, N_pad, desc->d, v, ws, st); })
+                       : hipSuccess;
     if (e == hipSuccess) {
         AttnArgs a{BH, N, N_pad, desc->d, softmax_scale(desc)};
         e = probed(LH_KERNEL_ATTN_FWD, st,
-                   [&] { return launch_attn_fwd(a, desc->dtype, q, k, ws, o32, o, lse, st); });
+                   [&] { return launch_attn_fwd(a, desc->dtype, q, k, f32 ? ws : v, o32, o, lse, st); });
     }
     return dev(e);
 }
@@ -273,22 +289,22 @@ lh_status dense_causal_attn_backward(const lh_desc* desc, const void* q, const v
     if (ws_bytes < P.dense_bwd_ws_bytes) return LH_E_WORKSPACE;
     hipStream_t st = (hipStream_t)stream;
     const int64_t BH = desc->B * desc->H, N = desc->N, N_pad = round64(N);
-    const size_t dT = align_up((size_t)BH * desc->d * N_pad * esize(desc->dtype));
-    void* qT = ws;
-    void* kT = at(ws, dT);
-    void* doT = at(ws, 2 * dT);
+    const size_t dT = dense_transposed_bytes(desc);
+    const bool f32 = desc->dtype == LH_F32;   // only the f32 kernels take Q^T, K^T, dO^T
+    void* qT = f32 ? ws : nullptr;
+    void* kT = f32 ? at(ws, dT) : nullptr;
+    void* doT = f32 ? at(ws, 2 * dT) : nullptr;
     float* nd = (float*)at(ws, 3 * dT);
     float* nl = (float*)at(ws, 3 * dT + align_up((size_t)BH * N * 4));
     const float* o32 = (const float*)at(fwd_ws, dT);
-    hipError_t e = launch_transpose(desc->dtype, BH, N, N_pad, desc->d, q, qT, st);
-    if (e == hipSuccess) e = launch_transpose(desc->dtype, BH, N, N_pad, desc->d, k, kT, st);
+    hipError_t e = f32 ? launch_transpose(desc->dtype, BH, N, N_pad, desc->d, q, qT, st) : hipSuccess;
+    if (e == hipSuccess && f32) e = launch_transpose(desc->dtype, BH, N, N_pad, desc->d, k, kT, st);
     if (e == hipSuccess)
         e = probed(LH_KERNEL_DENSE_PREP, st, [&] {
             return launch_dense_bwd_prep(desc->dtype, BH, N, N_pad, desc->d, dout, o32, lse, softmax_scale(desc),
                                          doT, nd, nl, st);
         });
     AttnArgs a{BH, N, N_pad, desc->d, softmax_scale(desc)};
-    const bool f32 = desc->dtype == LH_F32;
     if (e == hipSuccess)
         e = probed(LH_KERNEL_ATTN_DKDV, st, [&] {
             return launch_attn_dkdv(a, desc->dtype, f32, q, k, v, qT, dout, doT, nl, nd, dk, dv, st);

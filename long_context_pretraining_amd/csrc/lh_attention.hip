@@ -57,18 +57,22 @@ __device__ __forceinline__ void block_order(const AttnK& a, bool longest_last_ro
 // f32, and D = rowsum(dO * O) would then be off by ~2^-9 |dP| in rows
 // dominated by a few keys -- an error the products with K and Q magnify.
 template <typename T> constexpr bool kSplitP = sizeof(T) == 2;
+// bf16 products that contract over the sequence read their operand across the
+// rows of a row-major tile (tile_frag_tr); f32 reads a transposed copy.
+template <typename T> constexpr bool kTr = sizeof(T) == 2;
 
 // ---------------------------------------------------------------------------
 // Forward: O = softmax(scale Q K^T, causal) V and LSE, per 256-query block.
-// The output is written in f32 (and, when Ot is given, also in T).
+// The output is written in f32 (and, when Ot is given, also in T).  Vop is V
+// row-major [S][D] for bf16 and V^T [D][S_pad] for f32.
 // ---------------------------------------------------------------------------
 template <typename T, int D>
 __global__ __launch_bounds__(kThreads, (kBlocksPerCu<T, D>)) void attn_fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K,
-                                                            const T* __restrict__ VT, float* __restrict__ O32,
+                                                            const T* __restrict__ Vop, float* __restrict__ O32,
                                                             T* __restrict__ Ot, float* __restrict__ LSE, AttnK a) {
     typedef typename Frag<T>::type F;
-    constexpr int KROWB = D * (int)sizeof(T), VROWB = kBN * (int)sizeof(T);
-    constexpr int KBYTES = kBN * KROWB, VBYTES = D * VROWB, BUF = KBYTES + VBYTES;
+    constexpr int KROWB = D * (int)sizeof(T), VROWB = kTr<T> ? KROWB : kBN * (int)sizeof(T);
+    constexpr int KBYTES = kBN * KROWB, VBYTES = kTr<T> ? KBYTES : D * VROWB, BUF = KBYTES + VBYTES;
     extern __shared__ __align__(16) unsigned char smem[];
 
     int64_t bh; int qb;
@@ -78,7 +82,7 @@ __global__ __launch_bounds__(kThreads, (kBlocksPerCu<T, D>)) void attn_fwd_kerne
     const int64_t S = a.S;
     const T* Qh = Q + bh * S * D;
     const T* Kh = K + bh * S * D;
-    const T* VTh = VT + bh * D * a.S_pad;
+    const T* Vh = Vop + (kTr<T> ? bh * S * D : bh * D * a.S_pad);
 
     const int64_t q_blk0 = (int64_t)qb * kBlockRows;
     const int64_t q_base = q_blk0 + wave * kWaveRows;
@@ -110,12 +114,16 @@ __global__ __launch_bounds__(kThreads, (kBlocksPerCu<T, D>)) void attn_fwd_kerne
     const uint32_t col_stride = (uint32_t)(a.S_pad * sizeof(T));
     auto stage = [&](int t, unsigned char* b) {
         const uint32_t r0 = (uint32_t)t * kBN;
-        stage_tile<KROWB, KBYTES, 4>(b, Kh, [&](int r) {   // rows past S repeat row S - 1
+        auto rows = [&](int r) {   // rows past S repeat row S - 1
             const uint32_t row = r0 + r < last_row ? r0 + r : last_row;
             return row * (uint32_t)KROWB;
-        });
-        stage_tile<VROWB, VBYTES, 4>(b + KBYTES, reinterpret_cast<const unsigned char*>(VTh) + (int64_t)t * VROWB,
-                                     [&](int r) { return (uint32_t)r * col_stride; });
+        };
+        stage_tile<KROWB, KBYTES, 4>(b, Kh, rows);
+        if constexpr (kTr<T>)
+            stage_tile<KROWB, KBYTES, 4>(b + KBYTES, Vh, rows);
+        else
+            stage_tile<VROWB, VBYTES, 4>(b + KBYTES, reinterpret_cast<const unsigned char*>(Vh) + (int64_t)t * VROWB,
+                                         [&](int r) { return (uint32_t)r * col_stride; });
     };
     stage(0, smem);
     wait_tiles_and_sync();
@@ -191,7 +199,9 @@ __global__ __launch_bounds__(kThreads, (kBlocksPerCu<T, D>)) void attn_fwd_kerne
                     split_frag_vec<T>(s[ks][1], c2, p1, r1);
 #pragma unroll
                     for (int db = 0; db < D / 32; ++db) {
-                        const F vf = tile_frag<T, VROWB>(lv, 32 * db + col, 32 * ks + 16 * c2 + 8 * h);
+                        F vf;
+                        if constexpr (kTr<T>) vf = tile_frag_tr<KROWB>(lv, 32 * ks + 16 * c2, 32 * db);
+                        else vf = tile_frag<T, VROWB>(lv, 32 * db + col, 32 * ks + 16 * c2 + 8 * h);
                         mma_k16(o[0][db], vf, p0);
                         mma_k16(o[1][db], vf, p1);
                         if (kSplitP<T>) {
@@ -239,6 +249,12 @@ __global__ __launch_bounds__(kThreads, (kBlocksPerCu<T, D>)) void attn_fwd_kerne
 // sum; with dS rounded to 8 bits the remainder would carry 2^-9 |dS| |K| of
 // noise.  bf16 therefore feeds dS as hi + lo parts (as P in the forward).
 // ---------------------------------------------------------------------------
+template <typename T, int D>
+constexpr size_t dq_buf_bytes() {   // K and V row tiles (+ the K^T column tile for f32)
+    return 2 * kBN * D * sizeof(T) + (kTr<T> ? 0 : D * kBN * sizeof(T));
+}
+
+// KT (K^T [D][S_pad]) is read only by the f32 kernel; bf16 reads the K tile across its rows.
 template <typename T, int D, typename OutT>
 __global__ __launch_bounds__(kThreads, (kBlocksPerCu<T, D>)) void attn_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K,
                                                            const T* __restrict__ V, const T* __restrict__ KT,
@@ -247,7 +263,7 @@ __global__ __launch_bounds__(kThreads, (kBlocksPerCu<T, D>)) void attn_dq_kernel
                                                            AttnK a) {
     typedef typename Frag<T>::type F;
     constexpr int RROWB = D * (int)sizeof(T), CROWB = kBN * (int)sizeof(T);
-    constexpr int RBYTES = kBN * RROWB, CBYTES = D * CROWB, BUF = 2 * RBYTES + CBYTES;
+    constexpr int RBYTES = kBN * RROWB, BUF = (int)dq_buf_bytes<T, D>();
     extern __shared__ __align__(16) unsigned char smem[];
 
     int64_t bh; int qb;
@@ -258,7 +274,7 @@ __global__ __launch_bounds__(kThreads, (kBlocksPerCu<T, D>)) void attn_dq_kernel
     const T* Qh = Q + bh * S * D;
     const T* Kh = K + bh * S * D;
     const T* Vh = V + bh * S * D;
-    const T* KTh = KT + bh * D * a.S_pad;
+    const T* KTh = kTr<T> ? nullptr : KT + bh * D * a.S_pad;
     const T* dOh = dO + bh * S * D;
 
     const int64_t q_blk0 = (int64_t)qb * kBlockRows;
@@ -299,8 +315,10 @@ __global__ __launch_bounds__(kThreads, (kBlocksPerCu<T, D>)) void attn_dq_kernel
         };
         stage_tile<RROWB, RBYTES, 4>(b, Kh, rows);
         stage_tile<RROWB, RBYTES, 4>(b + RBYTES, Vh, rows);
-        stage_tile<CROWB, CBYTES, 4>(b + 2 * RBYTES, reinterpret_cast<const unsigned char*>(KTh) + (int64_t)t * CROWB,
-                                     [&](int r) { return (uint32_t)r * col_stride; });
+        if constexpr (!kTr<T>)
+            stage_tile<CROWB, D * CROWB, 4>(b + 2 * RBYTES,
+                                            reinterpret_cast<const unsigned char*>(KTh) + (int64_t)t * CROWB,
+                                            [&](int r) { return (uint32_t)r * col_stride; });
     };
     stage(0, smem);
     wait_tiles_and_sync();
@@ -348,7 +366,9 @@ __global__ __launch_bounds__(kThreads, (kBlocksPerCu<T, D>)) void attn_dq_kernel
                 split_frag<T>(s[1], c2, g1, r1);
 #pragma unroll
                 for (int db = 0; db < D / 32; ++db) {
-                    const F kf = tile_frag<T, CROWB>(lkt, 32 * db + col, 32 * ks + 16 * c2 + 8 * h);
+                    F kf;
+                    if constexpr (kTr<T>) kf = tile_frag_tr<RROWB>(lk, 32 * ks + 16 * c2, 32 * db);
+                    else kf = tile_frag<T, CROWB>(lkt, 32 * db + col, 32 * ks + 16 * c2 + 8 * h);
                     mma_k16(acc[0][db], kf, g0);
                     mma_k16(acc[1][db], kf, g1);
                     if (kSplitP<T>) {
@@ -389,7 +409,8 @@ __global__ __launch_bounds__(kThreads, (kBlocksPerCu<T, D>)) void attn_dq_kernel
 // computes step u+1's two score products (8 independent matrix products), so
 // the matrix cores and the vector units have independent work side by side.
 // LDS: query tiles of TQ rows.  Row tiles (Q, dO, -LSE/scale, -D) are needed
-// one step ahead and live in three buffers; column tiles (Q^T, dO^T) in two.
+// one step ahead and live in three buffers; for f32, column tiles (Q^T, dO^T)
+// in two (bf16 reads the Q and dO row tiles across their rows instead).
 // Tile t + 2's rows and tile t + 1's columns are loaded while tile t is used;
 // one barrier per tile.
 // ---------------------------------------------------------------------------
@@ -400,7 +421,7 @@ struct DkdvLds {
     static constexpr int RT = TQ * RROWB;              // one row tile
     static constexpr int CT = D * CROWB;               // one column tile
     static constexpr int RBUF = 2 * RT + 2 * 256;      // Q, dO, -LSE/scale, -D
-    static constexpr int CBUF = 2 * CT;                // Q^T, dO^T
+    static constexpr int CBUF = kTr<T> ? 0 : 2 * CT;  // Q^T, dO^T (f32 only)
     static constexpr int BYTES = 3 * RBUF + 2 * CBUF;
 };
 
@@ -425,9 +446,9 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_dkdv_kernel(const T* __restri
     const T* Qh = Q + bh * S * D;
     const T* Kh = K + bh * S * D;
     const T* Vh = V + bh * S * D;
-    const T* QTh = QT + bh * D * a.S_pad;
+    const T* QTh = kTr<T> ? nullptr : QT + bh * D * a.S_pad;
     const T* dOh = dO + bh * S * D;
-    const T* dOTh = dOT + bh * D * a.S_pad;
+    const T* dOTh = kTr<T> ? nullptr : dOT + bh * D * a.S_pad;
     const float* NLh = NL + bh * S;
     const float* NDh = ND + bh * S;
 
@@ -474,6 +495,7 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_dkdv_kernel(const T* __restri
         }
     };
     auto stage_cols = [&](int t) {
+        if constexpr (kTr<T>) return;
         unsigned char* b = cbuf(t);
         auto cols = [&](int r) { return (uint32_t)r * col_stride; };
         stage_tile<CROWB, L::CT, NW>(b, reinterpret_cast<const unsigned char*>(QTh) + (int64_t)t * CROWB, cols);
@@ -504,8 +526,9 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_dkdv_kernel(const T* __restri
             mma_k16(dp, da, vf[cc]);
         }
     };
-    // P, dS and the dV / dK products of one step (columns c0 .. c0+31 of column tile cb).
-    auto grads = [&](const unsigned char* cb, int c0, floatx16& sp, floatx16& dp) {
+    // P, dS and the dV / dK products of one step: queries c0 .. c0+31 of tile t,
+    // read across the rows of its row tile rb (bf16) or from its column tile cb (f32).
+    auto grads = [&](const unsigned char* rb, const unsigned char* cb, int c0, floatx16& sp, floatx16& dp) {
         const float c = a.scale_log2;
 #pragma unroll
         for (int c2 = 0; c2 < 2; ++c2) {
@@ -520,8 +543,14 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_dkdv_kernel(const T* __restri
             split_frag<T>(dp, c2, gh, gl);
 #pragma unroll
             for (int db = 0; db < D / 32; ++db) {
-                const F dof = tile_frag<T, CROWB>(cb + L::CT, 32 * db + col, c0 + 16 * c2 + 8 * h);
-                const F qtf = tile_frag<T, CROWB>(cb, 32 * db + col, c0 + 16 * c2 + 8 * h);
+                F dof, qtf;
+                if constexpr (kTr<T>) {
+                    dof = tile_frag_tr<RROWB>(rb + L::RT, c0 + 16 * c2, 32 * db);
+                    qtf = tile_frag_tr<RROWB>(rb, c0 + 16 * c2, 32 * db);
+                } else {
+                    dof = tile_frag<T, CROWB>(cb + L::CT, 32 * db + col, c0 + 16 * c2 + 8 * h);
+                    qtf = tile_frag<T, CROWB>(cb, 32 * db + col, c0 + 16 * c2 + 8 * h);
+                }
                 mma_k16(dv[db], dof, ph);
                 mma_k16(dk[db], qtf, gh);
                 if (kSplitP<T>) {
@@ -565,7 +594,7 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_dkdv_kernel(const T* __restri
         const int u = t * NSTEP + qs;
         const bool last_in_tile = qs + 1 == NSTEP;
         scores(last_in_tile ? rbuf(t + 1) : rbuf(t), last_in_tile ? 0 : 32 * (qs + 1), sp_n, dp_n);
-        grads(cbuf(t), 32 * qs, sp_c, dp_c);
+        grads(rbuf(t), cbuf(t), 32 * qs, sp_c, dp_c);
         if (needs_mask(u + 1)) {
             keep_branch();
             mask(sp_n, u + 1);
@@ -613,7 +642,7 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_dkdv_kernel(const T* __restri
 template <typename T, int D>
 size_t fwd_lds() { return 2 * 2 * kBN * D * sizeof(T); }
 template <typename T, int D>
-size_t dq_lds() { return 2 * 3 * kBN * D * sizeof(T); }
+size_t dq_lds() { return 2 * dq_buf_bytes<T, D>(); }
 
 AttnK make_k(const AttnArgs& a) {
     AttnK k{};
@@ -623,7 +652,7 @@ AttnK make_k(const AttnArgs& a) {
 }
 
 template <typename T, int D>
-hipError_t fwd_t(const AttnArgs& a, const void* Q, const void* K, const void* VT, float* O32, void* Ot, float* lse,
+hipError_t fwd_t(const AttnArgs& a, const void* Q, const void* K, const void* Vop, float* O32, void* Ot, float* lse,
                  hipStream_t st) {
     const AttnK k = make_k(a);
     const size_t sh = fwd_lds<T, D>();
@@ -631,7 +660,7 @@ hipError_t fwd_t(const AttnArgs& a, const void* Q, const void* K, const void* VT
         hipFuncSetAttribute((const void*)attn_fwd_kernel<T, D>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sh);
     (void)attr;
     attn_fwd_kernel<T, D><<<dim3((unsigned)(k.nblk * a.BH)), kThreads, sh, st>>>(
-        (const T*)Q, (const T*)K, (const T*)VT, O32, (T*)Ot, lse, k);
+        (const T*)Q, (const T*)K, (const T*)Vop, O32, (T*)Ot, lse, k);
     return hipGetLastError();
 }
 
@@ -672,11 +701,12 @@ hipError_t dq_t(const AttnArgs& a, const void* Q, const void* K, const void* V, 
 
 }  // namespace
 
-hipError_t launch_attn_fwd(const AttnArgs& a, int dtype, const void* Q, const void* K, const void* VT, float* O32,
+hipError_t launch_attn_fwd(const AttnArgs& a, int dtype, const void* Q, const void* K, const void* Vop, float* O32,
                            void* Ot, float* lse, hipStream_t st) {
     if (dtype == LH_BF16)
-        return a.d == 64 ? fwd_t<bf16, 64>(a, Q, K, VT, O32, Ot, lse, st) : fwd_t<bf16, 128>(a, Q, K, VT, O32, Ot, lse, st);
-    return fwd_t<float, 64>(a, Q, K, VT, O32, Ot, lse, st);   // f32 is built for d = 64 only
+        return a.d == 64 ? fwd_t<bf16, 64>(a, Q, K, Vop, O32, Ot, lse, st)
+                         : fwd_t<bf16, 128>(a, Q, K, Vop, O32, Ot, lse, st);
+    return fwd_t<float, 64>(a, Q, K, Vop, O32, Ot, lse, st);   // f32 is built for d = 64 only
 }
 
 hipError_t launch_attn_dkdv(const AttnArgs& a, int dtype, bool out_f32, const void* Q, const void* K, const void* V,

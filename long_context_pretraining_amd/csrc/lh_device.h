@@ -189,15 +189,20 @@ template <> struct V16<float> { typedef floatx4 type; enum { N = 4 }; };
 // LDS tiles.  A tile is ROWS rows of ROWB bytes, filled straight from global
 // memory by global_load_lds (16 bytes per lane, 1 KB per wave instruction, no
 // staging registers).  16-byte chunk c of row r sits at chunk c ^ f(r) of that
-// row, with f(r) = (r ^ (r >> 3)) & 7 for 128-byte rows and r & 15 for
-// 256-byte rows: lanes reading the same chunk of 8 consecutive rows then hit
-// 8 different 16-byte bank groups of a 128-byte bank window, and 16
-// consecutive rows 16 different groups of a 256-byte window.
-// The attention kernels' row tiles hold 64 rows of a row-major [S][D] array
-// (rows past S repeat row S-1; the masks make them irrelevant); their column
-// tiles hold D rows of a transposed [D][S_pad] array, 64 keys each, in the
-// slot order the gather and transposes write (see store_transposed): lane half
-// h then finds the 8 keys of its k16 step as one 16-byte run.  The projection
+// row.  f is a bijection on every aligned group of 8 (128-byte rows) or 16
+// (256-byte rows) rows, so lanes reading the same chunk of consecutive rows
+// hit distinct bank groups; it also sends 4 consecutive rows (128-byte rows:
+// rows r and r+2, which share banks) to disjoint sets of 4-chunk runs, so the
+// transpose loads of tile_frag_tr, which read 64 bytes of each of 4
+// consecutive rows, are conflict-free too:
+//   128-byte rows: f(r) = perm(r & 7) ^ ((r >> 3) & 7), perm swapping bits 1, 2
+//   256-byte rows: f(r) = ((r & 3) << 2) | ((r >> 2) & 3)
+// The attention kernels' row tiles hold 64 (or 32) rows of a row-major
+// [S][D] array (rows past S repeat row S-1; masks give them zero weight).  In
+// bf16 the products that contract over the sequence read those same row tiles
+// with tile_frag_tr; the f32 kernels instead take column tiles: D rows of a
+// transposed [D][S_pad] array, in the slot order store_transposed writes, so
+// that lane half h finds the keys of its k-step as one run.  The projection
 // GEMMs stage k-contiguous row tiles of both operands the same way.
 // ---------------------------------------------------------------------------
 typedef __attribute__((address_space(3))) void lds_void;
@@ -206,7 +211,8 @@ template <int ROWB>
 __device__ __forceinline__ int swz_key(int row) {
     static_assert(ROWB == 64 || ROWB == 128 || ROWB == 256, "row tiles of 64, 128 or 256 bytes");
     if (ROWB == 64) return ((row >> 1) ^ (row >> 3)) & 3;
-    return ROWB == 128 ? ((row ^ (row >> 3)) & 7) : (row & 15);
+    if (ROWB == 128) return ((row & 1) | ((row & 2) << 1) | ((row >> 1) & 2)) ^ ((row >> 3) & 7);
+    return ((row & 3) << 2) | ((row >> 2) & 3);
 }
 template <int ROWB>
 __device__ __forceinline__ int swz(int row, int chunk) { return row * ROWB + ((chunk ^ swz_key<ROWB>(row)) << 4); }
@@ -247,6 +253,29 @@ template <>
 __device__ __forceinline__ bf16x8 tile_frag<bf16, 256>(const unsigned char* tile, int row, int e0) {
     return *reinterpret_cast<const bf16x8*>(tile + swz<256>(row, e0 >> 3));
 }
+// 8 bf16 of one column of a row-major bf16 tile read across its rows with the
+// LDS transpose load: lane l gets column c0 + l % 32 of rows k0 + 4h + (0..3)
+// and k0 + 8 + 4h + (0..3), h = l / 32 -- the order in which the C tile of a
+// 32x32 product holds its rows, so a score tile can be the other operand of
+// a product that contracts over those rows without moving data between lanes.
+// (The transpose load gives lane j of each group of 16 lanes element j % 4 of
+// the 4-element runs addressed by lanes j/4, j/4 + 4, j/4 + 8 and j/4 + 12 of
+// its group; each lane below addresses the run its readers need.)
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+template <int ROWB>
+__device__ __forceinline__ bf16x8 tile_frag_tr(const unsigned char* tile, int k0, int c0) {
+    const int lane = threadIdx.x & 63, g = lane >> 4, s = lane & 15;
+    const int col = c0 + 16 * (g & 1) + 4 * (s & 3);
+    const int row = k0 + 4 * (g >> 1) + (s >> 2);
+    const int within = (col & 4) * 2;   // byte offset of the 4-element run inside its 16-byte chunk
+    const v4i16 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(tile + swz<ROWB>(row, col >> 3) + within));
+    const v4i16 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(tile + swz<ROWB>(row + 8, col >> 3) + within));
+    typedef short v8i16 __attribute__((ext_vector_type(8)));
+    const v8i16 r = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    return __builtin_bit_cast(bf16x8, r);
+}
+
 template <int ROWB>
 __device__ __forceinline__ floatx8 tile_frag_f32(const unsigned char* tile, int row, int e0) {
     const floatx4 a = *reinterpret_cast<const floatx4*>(tile + swz<ROWB>(row, e0 >> 2));

@@ -51,10 +51,12 @@ struct AttnArgs {
     int64_t BH, S, S_pad, d;
     float scale;
 };
-// O32: f32 output [BH,S,d] (always); Ot: optional copy in the input dtype (may be null)
-hipError_t launch_attn_fwd(const AttnArgs& a, int dtype, const void* Q, const void* K, const void* VT, float* O32,
+// O32: f32 output [BH,S,d] (always); Ot: optional copy in the input dtype (may be null).
+// Vop: V row-major [BH,S,d] for bf16, V^T [BH,d,S_pad] (store_transposed order) for f32.
+hipError_t launch_attn_fwd(const AttnArgs& a, int dtype, const void* Q, const void* K, const void* Vop, float* O32,
                            void* Ot, float* lse, hipStream_t st);
-// out_f32: dq/dk/dv are f32 (true) or the input dtype (false); nl = -LSE/scale, nd = -D per row
+// out_f32: dq/dk/dv are f32 (true) or the input dtype (false); nl = -LSE/scale, nd = -D per row.
+// QT, dOT, KT: transposed copies, read by the f32 kernels only (null for bf16).
 hipError_t launch_attn_dkdv(const AttnArgs& a, int dtype, bool out_f32, const void* Q, const void* K,
                             const void* V, const void* QT, const void* dO, const void* dOT, const float* nl,
                             const float* nd, void* dK, void* dV, hipStream_t st);

@@ -75,9 +75,10 @@ __device__ __forceinline__ void store_transposed(const T* tile, int ld, int64_t 
 }
 
 // ---------------------------------------------------------------------------
-// Gather: rows of the selected entries in slot order, row-major [S][d] and
-// transposed [d][S_pad] (columns past S are zero).  Level 0 rows come from
-// the input, coarser ones from the pyramid (pyramid row = flat id - N).
+// Gather: rows of the selected entries in slot order, row-major [S][d] and,
+// when c0..c2 are given (the f32 attention kernels take them), transposed
+// [d][S_pad] (columns past S are zero).  Level 0 rows come from the input,
+// coarser ones from the pyramid (pyramid row = flat id - N).
 // ---------------------------------------------------------------------------
 template <typename T>
 __global__ __launch_bounds__(kThreads) void gather_kernel(const T* __restrict__ q, const T* __restrict__ k,
@@ -93,6 +94,7 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(const T* __restrict__ 
     const T* srcp = pyr + (int64_t)z * G.BH * G.Mu * G.d;
     T* rows = z == 0 ? r0 : (z == 1 ? r1 : r2);
     T* cols = z == 0 ? c0 : (z == 1 ? c1 : c2);
+    const bool transposed = cols != nullptr;   // uniform over the grid
     const int64_t bh = blockIdx.y, s0 = (int64_t)blockIdx.x * kRows;
     const int ld = (int)G.d + VEC;
     const int nvec = (int)(G.d / VEC);
@@ -106,9 +108,11 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(const T* __restrict__ 
             val = *reinterpret_cast<const VT*>(src + vv * VEC);
             *reinterpret_cast<VT*>(rows + (bh * G.S + s) * G.d + vv * VEC) = val;
         }
+        if (transposed)
 #pragma unroll
-        for (int i = 0; i < VEC; ++i) tile[sl * ld + vv * VEC + i] = val[i];
+            for (int i = 0; i < VEC; ++i) tile[sl * ld + vv * VEC + i] = val[i];
     }
+    if (!transposed) return;
     __syncthreads();
     store_transposed(tile, ld, G.d, cols + bh * G.d * G.S_pad, G.S_pad, s0);
 }
@@ -328,8 +332,9 @@ __global__ __launch_bounds__(kThreads) void scatter_bwd_kernel(const T* __restri
             }
         }
         if (s < G.S) *reinterpret_cast<VT*>(dog + (bh * G.S + s) * G.d + vv * VEC) = r;
+        if (dogT)
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) tile[sl * ld + vv * VEC + e] = r[e];
+            for (int e = 0; e < VEC; ++e) tile[sl * ld + vv * VEC + e] = r[e];
         dpart[sl * nvec + vv] = dp;
     }
     __syncthreads();
@@ -342,7 +347,7 @@ __global__ __launch_bounds__(kThreads) void scatter_bwd_kernel(const T* __restri
             nl[bh * G.S + s] = -lse[bh * G.S + s] * inv_scale;
         }
     }
-    store_transposed(tile, ld, G.d, dogT + bh * G.d * G.S_pad, G.S_pad, s0);
+    if (dogT) store_transposed(tile, ld, G.d, dogT + bh * G.d * G.S_pad, G.S_pad, s0);
 }
 
 // ---------------------------------------------------------------------------
@@ -435,8 +440,9 @@ __global__ __launch_bounds__(kThreads) void dense_prep_kernel(const T* __restric
 #pragma unroll
             for (int e = 0; e < VEC; ++e) dp += to_f(val[e]) * ov[e];
         }
+        if (doT)
 #pragma unroll
-        for (int i = 0; i < VEC; ++i) tile[sl * ld + vv * VEC + i] = val[i];
+            for (int i = 0; i < VEC; ++i) tile[sl * ld + vv * VEC + i] = val[i];
         dpart[sl * nvec + vv] = dp;
     }
     __syncthreads();
@@ -448,7 +454,7 @@ __global__ __launch_bounds__(kThreads) void dense_prep_kernel(const T* __restric
             nl[bh * S + s0 + sl] = -lse[bh * S + s0 + sl] * inv_scale;
         }
     }
-    store_transposed(tile, ld, d, doT + bh * d * S_pad, S_pad, s0);
+    if (doT) store_transposed(tile, ld, d, doT + bh * d * S_pad, S_pad, s0);
 }
 
 inline unsigned blocks_for(int64_t n) { return (unsigned)((n + kRows - 1) / kRows); }
