@@ -667,8 +667,9 @@ hipError_t fwd_t(const AttnArgs& a, const void* Q, const void* K, const void* Vo
 template <typename T, int D, typename OutT>
 hipError_t dkdv_t(const AttnArgs& a, const void* Q, const void* K, const void* V, const void* QT, const void* dO,
                   const void* dOT, const float* nl, const float* nd, void* dK, void* dV, hipStream_t st) {
-    // 64-query tiles where three row and two column buffers fit the LDS twice over, else 32
-    constexpr int TQ = (D * sizeof(T) <= 128) ? 64 : 32;
+    // 64-query tiles, except f32 at 256-byte rows, whose three row and two
+    // column buffers would not fit: 32 there (bf16 has no column buffers)
+    constexpr int TQ = (kTr<T> || D * sizeof(T) <= 128) ? 64 : 32;
     typedef DkdvLds<T, D, TQ> L;
     static_assert(L::BYTES <= 160 * 1024, "dK/dV LDS budget");
     // d = 128 keeps twice the key and accumulator registers: one wave per SIMD
