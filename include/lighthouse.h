@@ -195,8 +195,8 @@ typedef struct {
     int64_t B, N, Dm, H, d;
 } lh_proj_desc;
 
-/* Backward workspace size (transposed copies of W, X and [dQ dK dV], and the
- * split partials of dW).  Host only. */
+/* Backward workspace size (a transposed copy of W and the split partials of
+ * dW).  Host only. */
 lh_status lh_qkv_plan(const lh_proj_desc* desc, size_t* bwd_ws_bytes);
 
 /* q = x Wq^T, k = x Wk^T, v = x Wv^T, written as [B, H, N, d] bf16 (the

@@ -339,8 +339,6 @@ lh_status proj_geom(const lh_proj_desc* d, ProjGeom* g) {
     G.splits = proj_splits(Nc, d->Dm, M);
     size_t off = 0;
     G.ws_wT = off; off += align_up((size_t)d->Dm * Nc * 2);
-    G.ws_xT = off; off += align_up((size_t)d->Dm * M * 2);
-    G.ws_gT = off; off += align_up((size_t)Nc * M * 2);
     G.ws_part = off; off += align_up((size_t)G.splits * Nc * d->Dm * 4);
     G.ws_bytes = off;
     *g = G;

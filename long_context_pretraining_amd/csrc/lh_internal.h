@@ -68,7 +68,7 @@ hipError_t launch_attn_dq(const AttnArgs& a, int dtype, bool out_f32, const void
 struct ProjGeom {
     int64_t B, N, Dm, H, d;
     int splits;                                  // k-splits of the dW product
-    size_t ws_wT, ws_xT, ws_gT, ws_part, ws_bytes;   // backward workspace layout (byte offsets)
+    size_t ws_wT, ws_part, ws_bytes;             // backward workspace layout (byte offsets)
 };
 hipError_t launch_qkv_forward(const ProjGeom& g, const void* x, const void* w, void* q, void* k, void* v,
                               hipStream_t st);

@@ -10,11 +10,12 @@
 //             dW = [dQ dK dV]^T X          [3Hd, Dm], summed over all B*N tokens, f32
 //
 // Q, K, V and their gradients are head-major [B,H,N,d], the layout of the
-// layer's inputs.  One GEMM kernel computes C = A B^T with both operands
-// k-contiguous (A [M x K], B [Nc x K]), so every matrix-core fragment is a
-// 16-byte run of one LDS-staged row; the backward builds the k-contiguous
-// operands it needs (W^T, X^T, [dQ dK dV]^T) with transposes.  The output
-// goes through LDS so that it leaves the block as 16-byte stores.
+// layer's inputs.  One GEMM kernel computes C = A B^T.  Its operands are
+// either k-contiguous (every matrix-core fragment a 16-byte run of one
+// LDS-staged row) or, for dW, whose k runs over the tokens, k-major: X and
+// [dQ dK dV] are staged as they lie and read across their rows with the LDS
+// transpose load.  The dX product takes W^T, made by a (6 MB) transpose.  The
+// output goes through LDS so that it leaves the block as 16-byte stores.
 #include "lh_device.h"
 #include "lh_internal.h"
 
@@ -33,11 +34,35 @@ constexpr int kCRows = 64, kCLd = kBN + 8;         // C leaves through LDS 64 ro
 constexpr int kGemmLds = (2 * 2 * kTileBytes > kCRows * kCLd * 4) ? 2 * 2 * kTileBytes : kCRows * kCLd * 4;
 static_assert(kBM == kBN, "one tile size for both operands");
 
-// Operand with k-contiguous rows: row r of k-block kb at kblock(kb) + r * row_bytes.
-struct RowMajorOp {
+// Operands.  Each stages the k-block kb of its 256 output rows base .. base+255
+// into one 32 KB LDS tile (stage) and says how the kernel reads fragments of
+// it (kKMajor).  k-contiguous operands store the tile as 256 rows of 64 k
+// (128-byte rows); k-major ones -- whose global rows run along k -- as four
+// sub-tiles of 64 k-rows x 64 output rows, read across their rows by the
+// transpose load.  Rows past the operand's end repeat its last row (or
+// 64-row block); the epilogue drops them.
+constexpr int kSubBytes = kBK * 64 * 2;   // one 64 x 64 bf16 sub-tile
+static_assert(4 * kSubBytes == kTileBytes, "four sub-tiles per operand tile");
+
+// k-contiguous rows: row r of k-block kb at kblock(kb) + r * row_bytes.
+template <class Self>
+struct KContiguous {
+    static constexpr bool kKMajor = false;
+    __device__ void stage(unsigned char* buf, int kb, uint32_t base) const {
+        const Self& o = *static_cast<const Self*>(this);
+        const uint32_t last = (uint32_t)(o.rows - 1), rb = o.row_bytes();
+        stage_tile<128, kTileBytes, kGWaves>(buf, o.kblock(kb), [&](int r) {
+            const uint32_t row = base + r < last ? base + r : last;
+            return row * rb;
+        });
+    }
+};
+struct RowMajorOp : KContiguous<RowMajorOp> {
     const bf16* p;
     int64_t ld;      // elements between rows
-    int64_t rows;    // valid rows (later rows repeat the last one)
+    int64_t rows;    // valid rows
+    RowMajorOp(const bf16* p_, int64_t ld_, int64_t rows_) : p(p_), ld(ld_), rows(rows_) {}
+    __device__ uint32_t row_bytes() const { return (uint32_t)(ld * 2); }
     __device__ const unsigned char* kblock(int kb) const {
         return reinterpret_cast<const unsigned char*>(p + (int64_t)kb * kBK);
     }
@@ -45,13 +70,16 @@ struct RowMajorOp {
 // [dQ dK dV] of one batch as rows = tokens, k = feature (which, h, dd): k-block
 // kb covers 64 features of one head.  32-bit index math: the source is picked
 // by comparisons, the head and the offset inside it by shifts (d = 64 or 128).
-struct HeadMajorOp {
+struct HeadMajorOp : KContiguous<HeadMajorOp> {
     const bf16 *x0, *x1, *x2;        // this batch's [H, N, d] slabs
     int kb_per_src;                   // H * d / 64
     int head_shift;                   // log2(d / 64)
     uint32_t head_stride;             // N * d elements
-    uint32_t row_bytes;               // d * 2
+    uint32_t rbytes;                  // d * 2
     int64_t rows;
+    HeadMajorOp(const bf16* a, const bf16* b, const bf16* c, int kps, int hs, uint32_t hst, uint32_t rb, int64_t r)
+        : x0(a), x1(b), x2(c), kb_per_src(kps), head_shift(hs), head_stride(hst), rbytes(rb), rows(r) {}
+    __device__ uint32_t row_bytes() const { return rbytes; }
     __device__ const unsigned char* kblock(int kb) const {
         const int which = (kb >= kb_per_src) + (kb >= 2 * kb_per_src);
         const int r = kb - which * kb_per_src;
@@ -60,9 +88,44 @@ struct HeadMajorOp {
         return reinterpret_cast<const unsigned char*>(x + (h * head_stride + dd));
     }
 };
-template <class Op> __device__ __forceinline__ uint32_t op_row_bytes(const Op& o);
-template <> __device__ __forceinline__ uint32_t op_row_bytes(const RowMajorOp& o) { return (uint32_t)(o.ld * 2); }
-template <> __device__ __forceinline__ uint32_t op_row_bytes(const HeadMajorOp& o) { return o.row_bytes; }
+// k-major: a row-major [K x cols] array (rows run along k), output row = column.
+struct KMajorOp {
+    static constexpr bool kKMajor = true;
+    const bf16* p;
+    int64_t ld;      // elements between k-rows
+    int cols;        // valid columns (a multiple of 64)
+    __device__ void stage(unsigned char* buf, int kb, uint32_t base) const {
+        const bf16* k0 = p + (int64_t)kb * kBK * ld;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int c0 = (int)base + 64 * j < cols ? (int)base + 64 * j : cols - 64;
+            stage_tile<128, kSubBytes, kGWaves>(buf + j * kSubBytes, k0 + c0,
+                                                [&](int r) { return (uint32_t)(r * ld * 2); });
+        }
+    }
+};
+// k-major [dQ dK dV]: k = tokens (all B*N of them), output row = feature
+// (which, h, dd); a 64-token k-block lies in one batch (N is a multiple of 64).
+struct HeadKMajorOp {
+    static constexpr bool kKMajor = true;
+    const bf16 *x0, *x1, *x2;   // [B, H, N, d]
+    int Hd, log2d, H;
+    uint32_t kb_per_batch;      // N / 64
+    uint32_t N;
+    __device__ void stage(unsigned char* buf, int kb, uint32_t base) const {
+        const uint32_t b = (uint32_t)kb / kb_per_batch, n0 = ((uint32_t)kb - b * kb_per_batch) * kBK;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int f0 = (int)base + 64 * j < 3 * Hd ? (int)base + 64 * j : 3 * Hd - 64;
+            const int which = (f0 >= Hd) + (f0 >= 2 * Hd);
+            const uint32_t f = (uint32_t)(f0 - which * Hd), h = f >> log2d, dd = f & ((1u << log2d) - 1);
+            const bf16* x = which == 0 ? x0 : (which == 1 ? x1 : x2);
+            const bf16* src = x + ((int64_t)(b * (uint32_t)H + h) * N + n0) * (1 << log2d) + dd;
+            stage_tile<128, kSubBytes, kGWaves>(buf + j * kSubBytes, src,
+                                                [&](int r) { return (uint32_t)r << (log2d + 1); });
+        }
+    }
+};
 
 // Epilogues: where 8 consecutive output columns n .. n+7 of row m go.
 struct QkvOut {                 // rows = tokens b*N + t, columns = features -> q/k/v [B,H,N,d]
@@ -119,17 +182,11 @@ __global__ __launch_bounds__(kGThreads, 1) void gemm_nt_kernel(OpA A, OpB B, Epi
     const int kb0 = blockIdx.z * kb_per_split;
     const int kb1 = kb0 + kb_per_split < nkb ? kb0 + kb_per_split : nkb;
 
-    const uint32_t a_rb = op_row_bytes(A), b_rb = op_row_bytes(B);
-    const uint32_t a_last = (uint32_t)(A.rows - 1), b_last = (uint32_t)(B.rows - 1);
+    static_assert(OpA::kKMajor == OpB::kKMajor, "both operands must present k in the same order");
+    constexpr bool KM = OpA::kKMajor;
     auto stage = [&](int kb, unsigned char* buf) {
-        stage_tile<128, kTileBytes, kGWaves>(buf, A.kblock(kb), [&](int r) {
-            const uint32_t row = (uint32_t)m0 + r < a_last ? (uint32_t)m0 + r : a_last;
-            return row * a_rb;
-        });
-        stage_tile<128, kTileBytes, kGWaves>(buf + kTileBytes, B.kblock(kb), [&](int r) {
-            const uint32_t row = (uint32_t)n0 + r < b_last ? (uint32_t)n0 + r : b_last;
-            return row * b_rb;
-        });
+        A.stage(buf, kb, (uint32_t)m0);
+        B.stage(buf + kTileBytes, kb, (uint32_t)n0);
     };
 
     constexpr int FI = kTM / 32, FJ = kTN / 32, NS = kBK / 16;
@@ -144,11 +201,16 @@ __global__ __launch_bounds__(kGThreads, 1) void gemm_nt_kernel(OpA A, OpB B, Epi
     // the next stage right after the barrier that makes it visible, so the
     // matrix cores never wait for a fresh LDS read at a stage boundary.
     bf16x8 fa[2][FI], fb[2][FJ];
+    // fragment of tile rows r0 .. r0+31 (a multiple of 32) for k16 step s
+    auto frag = [&](const unsigned char* t, int r0, int s) {
+        if constexpr (KM) return tile_frag_tr<128>(t + (r0 >> 6) * kSubBytes, 16 * s, r0 & 32);
+        else return tile_frag<bf16, 128>(t, r0 + col, 16 * s + 8 * h);
+    };
     auto read_frags = [&](const unsigned char* t, int s, bf16x8* a, bf16x8* b) {
 #pragma unroll
-        for (int i = 0; i < FI; ++i) a[i] = tile_frag<bf16, 128>(t, wm * kTM + 32 * i + col, 16 * s + 8 * h);
+        for (int i = 0; i < FI; ++i) a[i] = frag(t, wm * kTM + 32 * i, s);
 #pragma unroll
-        for (int j = 0; j < FJ; ++j) b[j] = tile_frag<bf16, 128>(t + kTileBytes, wn * kTN + 32 * j + col, 16 * s + 8 * h);
+        for (int j = 0; j < FJ; ++j) b[j] = frag(t + kTileBytes, wn * kTN + 32 * j, s);
     };
     auto products = [&](const bf16x8* a, const bf16x8* b) {
 #pragma unroll
@@ -162,9 +224,10 @@ __global__ __launch_bounds__(kGThreads, 1) void gemm_nt_kernel(OpA A, OpB B, Epi
     // loads in flight the compiler can only wait for every outstanding LDS
     // read; that wait now falls before the first product, when the reads it
     // covers were issued a whole substep earlier.
+    constexpr int READS = (KM ? 2 : 1) * (FI + FJ);   // a transpose-read fragment is two loads
     auto interleave = [] {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);             // matrix product
-        __builtin_amdgcn_sched_group_barrier(0x100, FI + FJ, 0);       // LDS reads
+        __builtin_amdgcn_sched_group_barrier(0x100, READS, 0);         // LDS reads
         __builtin_amdgcn_sched_group_barrier(0x008, FI * FJ - 1, 0);   // matrix products
     };
     static_assert(NS % 2 == 0, "substeps alternate between the two fragment sets");
@@ -312,8 +375,6 @@ hipError_t launch_qkv_backward(const ProjGeom& g, const void* x, const void* w, 
     const int64_t M = g.B * g.N, Nc = 3 * g.H * g.d, Dm = g.Dm;
     unsigned char* p = (unsigned char*)ws;
     bf16* wT = (bf16*)(p + g.ws_wT);      // [Dm x Nc]
-    bf16* xT = (bf16*)(p + g.ws_xT);      // [Dm x M]
-    bf16* gT = (bf16*)(p + g.ws_gT);      // [Nc x M]
     float* part = (float*)(p + g.ws_part);   // [splits][Nc x Dm]
     hipError_t e = transpose(TransposeSlabs{(const bf16*)w, nullptr, nullptr, wT, Nc, Dm, Dm, Nc, 1, 0, 0, 0}, 1, st);
     // dX = [dQ dK dV] W, per batch (rows: the batch's tokens)
@@ -325,23 +386,14 @@ hipError_t launch_qkv_backward(const ProjGeom& g, const void* x, const void* w, 
         RowMajorOut<bf16> E{(bf16*)dx + b * g.N * Dm, Dm, 0};
         e = gemm_nt<HeadMajorOp, RowMajorOp, RowMajorOut<bf16>, bf16>(A, B, E, g.N, Dm, Nc, 1, st);
     }
-    // X^T [Dm x M] and [dQ dK dV]^T [Nc x M]: every (source, b, h) slab [N x d] -> rows (src H + h) d.., cols b N..
-    if (e == hipSuccess)
-        e = transpose(TransposeSlabs{(const bf16*)x, nullptr, nullptr, xT, M, Dm, Dm, M, 1, 0, 0, 0}, 1, st);
-    // per batch b: slab z = (source, h) is the [N x d] block of head h, which lands in rows
-    // (source * H + h) * d .. and columns b * N .. of [dQ dK dV]^T
-    for (int64_t b = 0; b < g.B && e == hipSuccess; ++b) {
-        const int64_t off = b * g.H * g.N * g.d;
-        TransposeSlabs T{(const bf16*)dq + off, (const bf16*)dk + off, (const bf16*)dv + off, gT + b * g.N,
-                         g.N, g.d, g.d, M, (int)g.H, g.N * g.d, g.H * g.d * M, g.d * M};
-        e = transpose(T, (int)(3 * g.H), st);
-    }
-    // dW = [dQ dK dV]^T X over all tokens, split over k, partials summed in order
+    // dW = [dQ dK dV]^T X over all tokens: both operands are read k-major (rows
+    // along the tokens), split over k, partials summed in order
     if (e == hipSuccess) {
-        RowMajorOp A{gT, M, Nc};
-        RowMajorOp B{xT, M, Dm};
+        HeadKMajorOp A{(const bf16*)dq, (const bf16*)dk, (const bf16*)dv, (int)(g.H * g.d), g.d == 64 ? 6 : 7,
+                       (int)g.H, (uint32_t)(g.N / kBK), (uint32_t)g.N};
+        KMajorOp B{(const bf16*)x, Dm, (int)Dm};
         RowMajorOut<float> E{g.splits > 1 ? part : dw, Dm, Nc * Dm};
-        e = gemm_nt<RowMajorOp, RowMajorOp, RowMajorOut<float>, float>(A, B, E, Nc, Dm, M, g.splits, st);
+        e = gemm_nt<HeadKMajorOp, KMajorOp, RowMajorOut<float>, float>(A, B, E, Nc, Dm, M, g.splits, st);
     }
     if (e == hipSuccess && g.splits > 1) {
         const int64_t n = Nc * Dm;
