@@ -33,6 +33,7 @@ __device__ __forceinline__ V load_stream(const V* p) { return __builtin_nontempo
 struct PoolP {
     int64_t N, d, BH, Mu;
     int p, L, chunk, DS, nslices, nv_log2;   // DS / VEC = 1 << nv_log2 vectors per row slice
+    int sub;                      // tokens per level-1 pass: chunk, or a power of p >= p^2 dividing it
     int64_t offu[LH_MAX_LEVELS];  // row of level l inside a head's pyramid block
     int epc[LH_MAX_LEVELS];       // entries of level l per chunk (chunk / p^l)
 };
@@ -54,60 +55,98 @@ __global__ __launch_bounds__(kThreads) void pool_kernel(const T* __restrict__ x0
     const T* xh = x + bh * P.N * P.d;
     T* ph = pyr + ((int64_t)blockIdx.z * P.BH + bh) * P.Mu * P.d;
 
-    // Level 1 from the input: two entries per step, every child load issued
-    // before any is summed (children summed in index order, then / p).
-    const int n1 = len / P.p;
-    const int nt = n1 << P.nv_log2;
-    for (int ta = threadIdx.x; ta < nt; ta += 2 * kThreads) {
-        int task[2] = {ta, ta + kThreads};
-        float acc[2][VEC];
-        const T* src[2];
+    // The chunk is taken in passes of P.sub tokens: level 1 of the pass from
+    // the input into a scratch region of LDS, then (L > 2) its level-2
+    // entries into the chunk's level-2 array; levels 3 .. L-1 follow from
+    // that array.  (With P.sub = chunk this is one pass; smaller passes let
+    // whole rows fit the LDS when p^(L-1) is large.)
+    const int n1s = P.sub / P.p, n2 = len / (P.p * P.p);
+    float* l2 = lds + n1s * P.DS;   // level-2 array of the chunk
+    for (int sc = 0; sc < len; sc += P.sub) {
+        // Level 1 from the input: two entries per step, every child load issued
+        // before any is summed (children summed in index order, then / p).
+        const int n1 = (len - sc < P.sub ? len - sc : P.sub) / P.p;
+        const int e1 = sc / P.p;   // first level-1 entry of the pass
+        const int nt = n1 << P.nv_log2;
+        for (int ta = threadIdx.x; ta < nt; ta += 2 * kThreads) {
+            int task[2] = {ta, ta + kThreads};
+            float acc[2][VEC];
+            const T* src[2];
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int tk = task[j] < nt ? task[j] : ta;
-            src[j] = xh + (c0 + (int64_t)(tk >> P.nv_log2) * P.p) * P.d + dim0 + (tk & nvm) * VEC;
+            for (int j = 0; j < 2; ++j) {
+                const int tk = task[j] < nt ? task[j] : ta;
+                src[j] = xh + (c0 + sc + (int64_t)(tk >> P.nv_log2) * P.p) * P.d + dim0 + (tk & nvm) * VEC;
 #pragma unroll
-            for (int i = 0; i < VEC; ++i) acc[j][i] = 0.f;
-        }
-        for (int cb = 0; cb < P.p; cb += 4) {
-            VT v[2][4];
+                for (int i = 0; i < VEC; ++i) acc[j][i] = 0.f;
+            }
+            for (int cb = 0; cb < P.p; cb += 4) {
+                VT v[2][4];
 #pragma unroll
-            for (int u = 0; u < 4; ++u)
+                for (int u = 0; u < 4; ++u)
 #pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    v[j][u] = VT{};
-                    if (cb + u < P.p) v[j][u] = load_stream(reinterpret_cast<const VT*>(src[j] + (int64_t)(cb + u) * P.d));
+                    for (int j = 0; j < 2; ++j) {
+                        v[j][u] = VT{};
+                        if (cb + u < P.p)
+                            v[j][u] = load_stream(reinterpret_cast<const VT*>(src[j] + (int64_t)(cb + u) * P.d));
+                    }
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+                    if (cb + u < P.p)
+#pragma unroll
+                        for (int j = 0; j < 2; ++j)
+#pragma unroll
+                            for (int i = 0; i < VEC; ++i) acc[j][i] += to_f(v[j][u][i]);
+            }
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                if (task[j] >= nt) continue;
+                const int e = task[j] >> P.nv_log2, vv = task[j] & nvm;
+                VT out;
+#pragma unroll
+                for (int i = 0; i < VEC; ++i) {
+                    acc[j][i] = acc[j][i] / (float)P.p;
+                    out[i] = static_cast<T>(acc[j][i]);
                 }
+                if (P.L > 2) {
+                    float* dst = lds + e * P.DS + vv * VEC;
 #pragma unroll
-            for (int u = 0; u < 4; ++u)
-                if (cb + u < P.p)
-#pragma unroll
-                    for (int j = 0; j < 2; ++j)
-#pragma unroll
-                        for (int i = 0; i < VEC; ++i) acc[j][i] += to_f(v[j][u][i]);
+                    for (int i = 0; i < VEC; ++i) dst[i] = acc[j][i];
+                }
+                *reinterpret_cast<VT*>(ph + (P.offu[1] + (int64_t)cidx * P.epc[1] + e1 + e) * P.d + dim0 + vv * VEC) = out;
+            }
         }
+        if (P.L <= 2) continue;
+        __syncthreads();
+        // Level 2 of the pass from its level 1 in the scratch region.
+        const int e2 = sc / (P.p * P.p);
+        for (int task = threadIdx.x; task < ((n1 / P.p) << P.nv_log2); task += kThreads) {
+            const int e = task >> P.nv_log2, vv = task & nvm;
+            float acc[VEC];
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            if (task[j] >= nt) continue;
-            const int e = task[j] >> P.nv_log2, vv = task[j] & nvm;
+            for (int i = 0; i < VEC; ++i) acc[i] = 0.f;
+            for (int c = 0; c < P.p; ++c) {
+                const float* src = lds + (e * P.p + c) * P.DS + vv * VEC;
+#pragma unroll
+                for (int i = 0; i < VEC; ++i) acc[i] += src[i];
+            }
             VT out;
 #pragma unroll
             for (int i = 0; i < VEC; ++i) {
-                acc[j][i] = acc[j][i] / (float)P.p;
-                out[i] = static_cast<T>(acc[j][i]);
+                acc[i] = acc[i] / (float)P.p;
+                out[i] = static_cast<T>(acc[i]);
             }
-            if (P.L > 2) {
-                float* dst = lds + e * P.DS + vv * VEC;
+            if (P.L > 3) {
+                float* dst = l2 + (e2 + e) * P.DS + vv * VEC;
 #pragma unroll
-                for (int i = 0; i < VEC; ++i) dst[i] = acc[j][i];
+                for (int i = 0; i < VEC; ++i) dst[i] = acc[i];
             }
-            *reinterpret_cast<VT*>(ph + (P.offu[1] + (int64_t)cidx * P.epc[1] + e) * P.d + dim0 + vv * VEC) = out;
+            *reinterpret_cast<VT*>(ph + (P.offu[2] + (int64_t)cidx * P.epc[2] + e2 + e) * P.d + dim0 + vv * VEC) = out;
         }
+        __syncthreads();   // the scratch region is reused by the next pass
     }
-    __syncthreads();
-    // Levels 2 .. L-1 from the f32 level below, kept in LDS.
-    int prev_off = 0, cur_off = n1 * P.DS, n_prev = n1;
-    for (int l = 2; l < P.L; ++l) {
+    // Levels 3 .. L-1 from the f32 level below, kept in LDS.
+    int prev_off = n1s * P.DS, cur_off = prev_off + n2 * P.DS, n_prev = n2;
+    for (int l = 3; l < P.L; ++l) {
         const int n = n_prev / P.p;
         for (int task = threadIdx.x; task < (n << P.nv_log2); task += kThreads) {
             const int e = task >> P.nv_log2, vv = task & nvm;
@@ -456,20 +495,26 @@ hipError_t launch_pool(const LhGeom& g, int dtype, const void* q, const void* k,
     while (chunk < 256 && chunk * 2 <= g.N) chunk *= 2;
     // chunk must stay a multiple of p^(L-1): it is p^(L-1) * 2^j
     int DS = (int)g.d;
-    auto lds_bytes = [&](int64_t ch, int ds) {
-        int64_t ent = 0;
-        for (int l = 1; l < g.L; ++l) ent += ch / g.pw[l];
+    // f32 LDS: one pass's level 1 (sub / p entries) plus the chunk's levels 2 .. L-1
+    auto lds_bytes = [&](int64_t ch, int64_t sub, int ds) {
+        int64_t ent = sub / g.p;
+        for (int l = 2; l < g.L; ++l) ent += ch / g.pw[l];
         return ent * ds * 4;
     };
-    while (lds_bytes(chunk, DS) > 48 * 1024 && chunk > g.pw[g.L - 1]) chunk /= 2;
-    while (lds_bytes(chunk, DS) > 48 * 1024 && DS > VEC) DS /= 2;
-    if (lds_bytes(chunk, DS) > 64 * 1024) return hipErrorInvalidValue;
-    P.chunk = (int)chunk; P.DS = DS; P.nslices = (int)(g.d / DS);
+    constexpr int64_t kPoolLds = 48 * 1024;   // a few blocks per CU
+    while (lds_bytes(chunk, chunk, DS) > kPoolLds && chunk > g.pw[g.L - 1]) chunk /= 2;
+    // whole rows in passes of p^j tokens (j >= 2, dividing p^(L-1) and so the chunk) before slicing rows
+    int64_t sub = chunk;
+    for (int j = g.L - 2; j >= 2 && lds_bytes(chunk, sub, DS) > kPoolLds; --j) sub = g.pw[j];
+    if (lds_bytes(chunk, sub, DS) > kPoolLds) sub = chunk;
+    while (lds_bytes(chunk, sub, DS) > kPoolLds && DS > VEC) DS /= 2;
+    if (lds_bytes(chunk, sub, DS) > 64 * 1024) return hipErrorInvalidValue;
+    P.chunk = (int)chunk; P.sub = (int)sub; P.DS = DS; P.nslices = (int)(g.d / DS);
     while ((VEC << P.nv_log2) < DS) ++P.nv_log2;
     if ((VEC << P.nv_log2) != DS) return hipErrorInvalidValue;
     for (int l = 0; l < g.L; ++l) P.epc[l] = (int)(chunk / g.pw[l]);
     dim3 grid((unsigned)(ceil_div(g.N, chunk) * P.nslices), (unsigned)g.BH, 3);
-    size_t sh = (size_t)lds_bytes(chunk, DS);
+    size_t sh = (size_t)lds_bytes(chunk, sub, DS);
     if (dtype == LH_BF16)
         pool_kernel<bf16><<<grid, kThreads, sh, st>>>((const bf16*)q, (const bf16*)k, (const bf16*)v, (bf16*)pyr, P);
     else
