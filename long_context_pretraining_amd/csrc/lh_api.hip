@@ -228,7 +228,7 @@ lh_status lh_backward(const lh_desc* desc, const int32_t* gidx, const int32_t* g
     float* dxg[3] = {(float*)at(bwd_ws, P.bwd_off[LH_BWD_DQ]), (float*)at(bwd_ws, P.bwd_off[LH_BWD_DK]),
                      (float*)at(bwd_ws, P.bwd_off[LH_BWD_DV])};
     hipError_t e = probed(LH_KERNEL_SCATTER_BWD, st, [&] {
-        return launch_scatter_bwd(g, desc->dtype, dout, og, gidx, lse, softmax_scale(desc), dog, dogT, nd, nl,
+        return launch_scatter_bwd(g, desc->dtype, dout, og, gidx, gpos, lse, softmax_scale(desc), dog, dogT, nd, nl,
                                   st);
     });
     const void* Qg = at(fwd_ws, P.fwd_off[LH_FWD_QG]);

@@ -35,9 +35,10 @@ hipError_t launch_scatter_fwd(const LhGeom& g, int dtype, const float* og, const
                               hipStream_t st);
 // also writes nd = -rowsum(dOg * Og) and nl = -lse / scale, the backward's
 // per-row offsets of dP and of the raw scores
+// (dogT: the transposed copy, f32 only, else null)
 hipError_t launch_scatter_bwd(const LhGeom& g, int dtype, const void* dout, const float* og,
-                              const int32_t* gidx, const float* lse, float scale, void* dog, void* dogT,
-                              float* nd, float* nl, hipStream_t st);
+                              const int32_t* gidx, const int32_t* gpos, const float* lse, float scale, void* dog,
+                              void* dogT, float* nd, float* nl, hipStream_t st);
 hipError_t launch_gather_pool_bwd(const LhGeom& g, int dtype, const float* const dx_g[3], const int32_t* gpos,
                                   void* const dx[3], hipStream_t st);
 hipError_t launch_transpose(int dtype, int64_t BH, int64_t S, int64_t S_pad, int64_t d, const void* x,

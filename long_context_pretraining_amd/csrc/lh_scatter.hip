@@ -397,6 +397,202 @@ __global__ __launch_bounds__(kThreads) void gpool_bwd_kernel(const float* __rest
 // Dense-baseline helpers: transpose x [S][d] -> xT [d][S_pad] (zero columns
 // past S), and the backward prologue (transposed dO and D = rowsum(dO * O)).
 // ---------------------------------------------------------------------------
+// ---------------------------------------------------------------------------
+// Scatter backward as a pyramid (the form used when whole rows fit the LDS).
+// With t' = t + 1, the range R(l, i) = [(i+1) p^l - 1, (i+2) p^l - 2] is the
+// aligned block i+1 of level l of the shifted sequence dout'[t'] = dout[t'-1]
+// (dout'[0] = 0, and tokens past N - 1 are 0, which is the clipping), so every
+// range sum is an entry of the plain sum pyramid of dout': children summed in
+// index order in f32, level by level.  A block builds that pyramid for one
+// aligned chunk of t' in LDS -- level 1 in passes of P.sub tokens, like the
+// pooling pass -- and stores every entry whose slot is selected as dOg (one
+// rounding to T).  dout is read once instead of once per covering level.
+// D and -LSE/scale follow in slot order (slot_dot_kernel).
+// ---------------------------------------------------------------------------
+struct ShiftP {
+    int chunk;   // t' positions per block: a multiple of p^(L-1)
+    int sub;     // t' positions per level-1 pass: chunk, or p^j (j >= 2) dividing it
+};
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void scatter_bwd_pyr_kernel(const T* __restrict__ dout,
+                                                                   const int32_t* __restrict__ gpos,
+                                                                   T* __restrict__ dog, MapGeo G, ShiftP P) {
+    extern __shared__ __align__(16) float lds[];
+    constexpr int VEC = V16<T>::N;
+    typedef typename V16<T>::type VT;
+    const int d = (int)G.d, nvec = d / VEC, p = G.p;
+    const int64_t bh = blockIdx.y;
+    const int64_t c0 = (int64_t)blockIdx.x * P.chunk;   // first t' of the chunk
+    const T* dh = dout + bh * G.N * G.d;
+    T* dgh = dog + bh * G.S * G.d;
+    const int32_t* gp = gpos + bh * G.M_total;
+
+    // entry (l, k) of the shifted pyramid is range entry i = k - 1
+    auto slot_of = [&](int l, int64_t k) {
+        const int64_t i = k - 1;
+        return i >= 0 && i < G.off[l + 1] - G.off[l] ? gp[G.off[l] + i] : -1;
+    };
+    auto store = [&](int32_t slot, int vv, const float* acc) {
+        VT r;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) r[e] = static_cast<T>(acc[e]);
+        *reinterpret_cast<VT*>(dgh + (int64_t)slot * G.d + vv * VEC) = r;
+    };
+    auto load_row = [&](int64_t tp, int vv, float* x) {   // dout'[tp], 0 outside [1, N]
+        VT v = {};
+        if (tp >= 1 && tp <= G.N) v = *reinterpret_cast<const VT*>(dh + (tp - 1) * G.d + vv * VEC);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) x[e] = to_f(v[e]);
+    };
+
+    if (G.L < 2) {   // level 0 only: every selected token copied
+        for (int task = threadIdx.x; task < P.chunk * nvec; task += kThreads) {
+            const int e = task / nvec, vv = task % nvec;
+            const int32_t slot = slot_of(0, c0 + e);
+            float x[VEC];
+            load_row(c0 + e, vv, x);
+            if (slot >= 0) store(slot, vv, x);
+        }
+        return;
+    }
+    const int n1s = P.sub / p, n2 = P.chunk / (p * p);
+    float* l2 = lds + n1s * d;
+    for (int sc = 0; sc < P.chunk; sc += P.sub) {
+        // level 1 of the pass (and the level-0 tokens it reads): two entries per
+        // step, their children in batches of 4, every row load and slot lookup
+        // issued before any is used
+        const int64_t k1 = (c0 + sc) / p;
+        const int nt = n1s * nvec;
+        for (int ta = threadIdx.x; ta < nt; ta += 2 * kThreads) {
+            const int task[2] = {ta, ta + kThreads < nt ? ta + kThreads : ta};
+            const bool live1 = ta + kThreads < nt;
+            int e[2], vv[2];
+            int32_t s1[2];
+            float acc[2][VEC];
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                e[j] = task[j] / nvec;
+                vv[j] = task[j] % nvec;
+                s1[j] = slot_of(1, k1 + e[j]);
+#pragma unroll
+                for (int i = 0; i < VEC; ++i) acc[j][i] = 0.f;
+            }
+            for (int cb = 0; cb < p; cb += 4) {
+                float x[2][4][VEC];
+                int32_t s0[2][4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+#pragma unroll
+                    for (int j = 0; j < 2; ++j) {
+                        const int64_t tp = (k1 + e[j]) * p + cb + u;
+                        s0[j][u] = -1;
+                        if (cb + u < p) {
+                            load_row(tp, vv[j], x[j][u]);
+                            s0[j][u] = slot_of(0, tp);
+                        }
+                    }
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+#pragma unroll
+                    for (int j = 0; j < 2; ++j)
+                        if (cb + u < p) {
+#pragma unroll
+                            for (int i = 0; i < VEC; ++i) acc[j][i] += x[j][u][i];
+                            if (s0[j][u] >= 0 && (j == 0 || live1)) store(s0[j][u], vv[j], x[j][u]);
+                        }
+            }
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                if (j == 1 && !live1) continue;
+                if (G.L > 2)
+#pragma unroll
+                    for (int i = 0; i < VEC; ++i) lds[e[j] * d + vv[j] * VEC + i] = acc[j][i];
+                if (s1[j] >= 0) store(s1[j], vv[j], acc[j]);
+            }
+        }
+        if (G.L <= 2) continue;
+        __syncthreads();
+        const int64_t k2 = (c0 + sc) / (p * p);
+        const int e2 = sc / (p * p);
+        for (int task = threadIdx.x; task < (n1s / p) * nvec; task += kThreads) {
+            const int e = task / nvec, vv = task % nvec;
+            const int32_t s2 = slot_of(2, k2 + e);
+            float acc[VEC];
+#pragma unroll
+            for (int i = 0; i < VEC; ++i) acc[i] = 0.f;
+            for (int c = 0; c < p; ++c)
+#pragma unroll
+                for (int i = 0; i < VEC; ++i) acc[i] += lds[(e * p + c) * d + vv * VEC + i];
+            if (G.L > 3)
+#pragma unroll
+                for (int i = 0; i < VEC; ++i) l2[(e2 + e) * d + vv * VEC + i] = acc[i];
+            if (s2 >= 0) store(s2, vv, acc);
+        }
+        __syncthreads();   // the level-1 scratch is reused by the next pass
+    }
+    // levels 3 .. L-1 from the level below, kept in LDS
+    int prev_off = n1s * d, cur_off = prev_off + n2 * d, n_prev = n2;
+    for (int l = 3; l < G.L; ++l) {
+        const int n = n_prev / p;
+        const int64_t kl = c0 / G.pw[l];
+        for (int task = threadIdx.x; task < n * nvec; task += kThreads) {
+            const int e = task / nvec, vv = task % nvec;
+            const int32_t sl = slot_of(l, kl + e);
+            float acc[VEC];
+#pragma unroll
+            for (int i = 0; i < VEC; ++i) acc[i] = 0.f;
+            for (int c = 0; c < p; ++c)
+#pragma unroll
+                for (int i = 0; i < VEC; ++i) acc[i] += lds[prev_off + (e * p + c) * d + vv * VEC + i];
+            if (l + 1 < G.L)
+#pragma unroll
+                for (int i = 0; i < VEC; ++i) lds[cur_off + e * d + vv * VEC + i] = acc[i];
+            if (sl >= 0) store(sl, vv, acc);
+        }
+        __syncthreads();
+        prev_off = cur_off;
+        cur_off += n * d;
+        n_prev = n;
+    }
+}
+
+// D[g] = dOg[g] . Og[g] (f32; per lane VEC products in order, then the lanes
+// of the row in order -- the order of the dense path) and -LSE/scale, per slot.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void slot_dot_kernel(const T* __restrict__ dog, const float* __restrict__ og,
+                                                            const float* __restrict__ lse, float inv_scale,
+                                                            float* __restrict__ nd, float* __restrict__ nl,
+                                                            int64_t S, int64_t d) {
+    constexpr int VEC = V16<T>::N;
+    typedef typename V16<T>::type VT;
+    __shared__ float dpart[kRows * 32];
+    const int nvec = (int)(d / VEC);
+    const int64_t bh = blockIdx.y, s0 = (int64_t)blockIdx.x * kRows;
+    for (int task = threadIdx.x; task < kRows * nvec; task += kThreads) {
+        const int sl = task / nvec, vv = task - sl * nvec;
+        float dp = 0.f;
+        if (s0 + sl < S) {
+            const int64_t row = (bh * S + s0 + sl) * d + vv * VEC;
+            const VT v = *reinterpret_cast<const VT*>(dog + row);
+            const float* ov = og + row;
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) dp += to_f(v[e]) * ov[e];
+        }
+        dpart[sl * nvec + vv] = dp;
+    }
+    __syncthreads();
+    for (int sl = threadIdx.x; sl < kRows; sl += kThreads) {
+        const int64_t s = s0 + sl;
+        if (s < S) {
+            float acc = 0.f;
+            for (int vv = 0; vv < nvec; ++vv) acc += dpart[sl * nvec + vv];
+            nd[bh * S + s] = -acc;
+            nl[bh * S + s] = -lse[bh * S + s] * inv_scale;
+        }
+    }
+}
+
 template <typename T>
 __global__ __launch_bounds__(kThreads) void transpose_kernel(const T* __restrict__ x, T* xT, int64_t S,
                                                              int64_t S_pad, int64_t d) {
@@ -507,10 +703,57 @@ hipError_t launch_scatter_fwd(const LhGeom& g, int dtype, const float* og, const
     });
 }
 
+namespace {
+// Chunk and level-1 pass of the pyramid form of the scatter backward: whole
+// rows of f32 in at most 48 KB of LDS (one pass's level 1 plus the chunk's
+// levels 2 .. L-1).  chunk = 0 when no choice fits.
+ShiftP shift_plan(const LhGeom& g) {
+    auto bytes = [&](int64_t ch, int64_t sub) {
+        int64_t ent = g.L > 2 ? sub / g.p : 0;
+        for (int l = 2; l < g.L - 1; ++l) ent += ch / g.pw[l];   // the coarsest level is not kept
+        return ent * g.d * 4;
+    };
+    constexpr int64_t kMax = 48 * 1024;
+    int64_t chunk = g.pw[g.L - 1];
+    while (chunk < 256) chunk *= 2;
+    while (bytes(chunk, chunk) > kMax && chunk > g.pw[g.L - 1]) chunk /= 2;
+    int64_t sub = chunk;
+    for (int j = g.L - 2; j >= 2 && bytes(chunk, sub) > kMax; --j) sub = g.pw[j];
+    if (bytes(chunk, sub) > kMax || chunk > (1 << 20)) return ShiftP{0, 0};
+    return ShiftP{(int)chunk, (int)sub};
+}
+}  // namespace
+
 hipError_t launch_scatter_bwd(const LhGeom& g, int dtype, const void* dout, const float* og, const int32_t* gidx,
-                              const float* lse, float scale, void* dog, void* dogT, float* nd, float* nl,
-                              hipStream_t st) {
+                              const int32_t* gpos, const float* lse, float scale, void* dog, void* dogT, float* nd,
+                              float* nl, hipStream_t st) {
     const MapGeo G = make_geo(g);
+    const ShiftP SP = shift_plan(g);
+    if (SP.chunk > 0) {
+        // pyramid form: every t' in [0, N] lies in one of the chunks
+        dim3 grid((unsigned)(g.N / SP.chunk + 1), (unsigned)g.BH);
+        int64_t ent = g.L > 2 ? SP.sub / g.p : 0;
+        for (int l = 2; l < g.L - 1; ++l) ent += SP.chunk / g.pw[l];
+        const size_t sh = (size_t)ent * g.d * 4;
+        if (dtype == LH_BF16)
+            scatter_bwd_pyr_kernel<bf16><<<grid, kThreads, sh, st>>>((const bf16*)dout, gpos, (bf16*)dog, G, SP);
+        else
+            scatter_bwd_pyr_kernel<float><<<grid, kThreads, sh, st>>>((const float*)dout, gpos, (float*)dog, G, SP);
+        dim3 sg((unsigned)(g.S_pad / kRows), (unsigned)g.BH);
+        if (dtype == LH_BF16)
+            slot_dot_kernel<bf16><<<sg, kThreads, 0, st>>>((const bf16*)dog, og, lse, 1.f / scale, nd, nl, g.S, g.d);
+        else
+            slot_dot_kernel<float><<<sg, kThreads, 0, st>>>((const float*)dog, og, lse, 1.f / scale, nd, nl, g.S,
+                                                            g.d);
+        hipError_t e = hipGetLastError();
+        if (e == hipSuccess && dogT) {   // f32 attention kernels take dOg transposed
+            dim3 tg((unsigned)(g.S_pad / kRows), (unsigned)g.BH);
+            transpose_kernel<float><<<tg, kThreads, tile_bytes<float>(g.d), st>>>((const float*)dog, (float*)dogT,
+                                                                                   g.S, g.S_pad, g.d);
+            e = hipGetLastError();
+        }
+        return e;
+    }
     dim3 grid((unsigned)(g.S_pad / kRows), (unsigned)g.BH);
     if (dtype == LH_BF16) {
         const size_t sh = tile_bytes<bf16>(g.d) + 4 * kRows * (g.d / 8);

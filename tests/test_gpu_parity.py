@@ -24,6 +24,9 @@ SMALL = [
     W("minimal_bf16", 1, 1, 16, 64, "bf16", 4, 3, 1, 107, False),    # N = p^(L-1), S = 9
     W("L2_bf16", 1, 2, 512, 64, "bf16", 4, 2, 40, 105, True),
     W("p2_L8_bf16", 1, 1, 2048, 64, "bf16", 2, 8, 5, 108, True),     # deepest pyramid
+    # p^(L-1) = 4096: whole f32 rows of a chunk's pyramid exceed the LDS, so the scatter
+    # backward takes its slot-centric form and pooling slices rows
+    W("p4_L7_bf16", 1, 1, 8192, 64, "bf16", 4, 7, 2, 109, True),
 ]
 
 
