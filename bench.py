@@ -58,14 +58,17 @@ SOURCE_GROUPS = {
     "proj": [_CSRC + "lh_proj.hip", _CSRC + "lh_device.h", _CSRC + "lh_internal.h"],
 }
 ATTN_SOURCES = SOURCE_GROUPS["attn"]
-# bench name -> kernel symbol as the profiles name it, and its source group
+# bench name -> the kernel symbols (as the profiles name them) its call launches, and their source group
 KERNEL_SYMBOLS = {
-    "pool": ("pool_kernel", "select"), "score": ("score_kernel", "select"), "topk": ("topk_kernel", "select"),
-    "map": ("map_kernel", "select"), "gather": ("gather_kernel", "scatter"),
-    "attn_fwd": ("attn_fwd_kernel", "attn"), "scatter_fwd": ("scatter_fwd_kernel", "scatter"),
-    "scatter_bwd": ("scatter_bwd_kernel", "scatter"), "attn_dkdv": ("attn_dkdv_kernel", "attn"),
-    "attn_dq": ("attn_dq_kernel", "attn"), "gather_pool_bwd": ("gpool_bwd_kernel", "scatter"),
+    "pool": (("pool_kernel",), "select"), "score": (("score_kernel",), "select"),
+    "topk": (("topk_kernel",), "select"), "map": (("map_kernel",), "select"),
+    "gather": (("gather_kernel",), "scatter"), "attn_fwd": (("attn_fwd_kernel",), "attn"),
+    "scatter_fwd": (("scatter_fwd_kernel",), "scatter"),
+    "scatter_bwd": (("scatter_bwd_pyr_kernel", "slot_dot_kernel"), "scatter"),
+    "attn_dkdv": (("attn_dkdv_kernel",), "attn"), "attn_dq": (("attn_dq_kernel",), "attn"),
+    "gather_pool_bwd": (("gpool_bwd_kernel",), "scatter"),
 }
+SCATTER_EXTRA = ("scatter_bwd_kernel", "transpose_kernel")   # other forms / f32 helpers of the scatter group
 TRAFFIC_PROFILE = "profiles/lighthouse_98k_k1536_hbm_traffic.md"
 
 
@@ -80,9 +83,11 @@ def sources_sha256(paths):
 
 
 def symbol_group(symbol):
-    for sym, group in KERNEL_SYMBOLS.values():
-        if sym == symbol:
+    for syms, group in KERNEL_SYMBOLS.values():
+        if symbol in syms:
             return group
+    if symbol in SCATTER_EXTRA:
+        return "scatter"
     if symbol.startswith("gemm_nt_kernel") or symbol in ("transpose_slabs_kernel", "reduce_splits_kernel"):
         return "proj"
     return None
@@ -95,7 +100,7 @@ def stored_traffic(kernel, workload="llama530m_98k_k1536"):
     another one, or the kernel's sources changed since."""
     if workload != "llama530m_98k_k1536" or kernel not in KERNEL_SYMBOLS:
         return None
-    symbol, group = KERNEL_SYMBOLS[kernel]
+    symbols, group = KERNEL_SYMBOLS[kernel]
     root = os.path.dirname(os.path.abspath(__file__))
     path = os.path.join(root, TRAFFIC_PROFILE)
     if not os.path.exists(path):
@@ -108,8 +113,8 @@ def stored_traffic(kernel, workload="llama530m_98k_k1536"):
                 fields[key.strip()] = val.strip().strip("`")
     if fields.get(f"sources_sha256.{group}") != sources_sha256(SOURCE_GROUPS[group]):
         return None
-    val = fields.get(f"hbm_bytes_per_launch.{symbol}")
-    return int(val) if val is not None else None
+    vals = [fields.get(f"hbm_bytes_per_launch.{sym}") for sym in symbols]
+    return sum(int(v) for v in vals) if all(v is not None for v in vals) else None
 
 
 # the three instantiations of the projection GEMM, told apart by their operand / epilogue types

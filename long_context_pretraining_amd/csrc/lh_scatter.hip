@@ -729,7 +729,14 @@ hipError_t launch_scatter_bwd(const LhGeom& g, int dtype, const void* dout, cons
                               float* nl, hipStream_t st) {
     const MapGeo G = make_geo(g);
     const ShiftP SP = shift_plan(g);
-    if (SP.chunk > 0) {
+    // The slot-centric form reads each selected entry's range: sum over levels of
+    // (selected entries) x p^l rows, i.e. p k_(l+1) entries at l < L-1 and all M_(L-1)
+    // at the top.  The pyramid form reads dO once but in short, latency-bound blocks;
+    // measured, it wins once the slot form re-reads dO about 2.75 times or more
+    // (512K tokens, L = 6: 3.0x, 0.72 -> 0.36 ms) and ties at 2.3x (98K, L = 4).
+    int64_t rows = g.M[g.L - 1] * g.pw[g.L - 1];
+    for (int l = 0; l + 1 < g.L; ++l) rows += g.p * g.k_eff[l + 1] * g.pw[l];
+    if (SP.chunk > 0 && 4 * rows >= 11 * g.N) {
         // pyramid form: every t' in [0, N] lies in one of the chunks
         dim3 grid((unsigned)(g.N / SP.chunk + 1), (unsigned)g.BH);
         int64_t ent = g.L > 2 ? SP.sub / g.p : 0;

@@ -27,6 +27,11 @@ SMALL = [
     # p^(L-1) = 4096: whole f32 rows of a chunk's pyramid exceed the LDS, so the scatter
     # backward takes its slot-centric form and pooling slices rows
     W("p4_L7_bf16", 1, 1, 8192, 64, "bf16", 4, 7, 2, 109, True),
+    # large k against small coarse levels: the per-slot ranges would re-read dO ~3.5x, so the
+    # scatter backward takes its pyramid form (f32: with the transposed copy; p = 3, d = 128:
+    # a partial last chunk)
+    W("pyr_f32", 1, 2, 2048, 64, "f32", 4, 4, 256, 110, False),
+    W("pyr_p3_d128_bf16", 1, 2, 1350, 128, "bf16", 3, 4, 200, 111, True),
 ]
 
 
