@@ -58,17 +58,24 @@ SOURCE_GROUPS = {
     "proj": [_CSRC + "lh_proj.hip", _CSRC + "lh_device.h", _CSRC + "lh_internal.h"],
 }
 ATTN_SOURCES = SOURCE_GROUPS["attn"]
-# bench name -> the kernel symbols (as the profiles name them) its call launches, and their source group
+# bench name -> the kernel symbols (as the profiles name them) its call launches, and their source
+# group; a call with several forms lists each form's symbols (the first form found in a profile counts)
 KERNEL_SYMBOLS = {
     "pool": (("pool_kernel",), "select"), "score": (("score_kernel",), "select"),
     "topk": (("topk_kernel",), "select"), "map": (("map_kernel",), "select"),
     "gather": (("gather_kernel",), "scatter"), "attn_fwd": (("attn_fwd_kernel",), "attn"),
     "scatter_fwd": (("scatter_fwd_kernel",), "scatter"),
-    "scatter_bwd": (("scatter_bwd_pyr_kernel", "slot_dot_kernel"), "scatter"),
+    "scatter_bwd": ((("scatter_bwd_kernel",), ("scatter_bwd_pyr_kernel", "slot_dot_kernel")), "scatter"),
     "attn_dkdv": (("attn_dkdv_kernel",), "attn"), "attn_dq": (("attn_dq_kernel",), "attn"),
     "gather_pool_bwd": (("gpool_bwd_kernel",), "scatter"),
 }
-SCATTER_EXTRA = ("scatter_bwd_kernel", "transpose_kernel")   # other forms / f32 helpers of the scatter group
+SCATTER_EXTRA = ("transpose_kernel",)   # f32 helper of the scatter group
+
+
+def kernel_forms(kernel):
+    """The alternative symbol tuples of bench kernel `kernel`."""
+    syms = KERNEL_SYMBOLS[kernel][0]
+    return syms if isinstance(syms[0], tuple) else (syms,)
 TRAFFIC_PROFILE = "profiles/lighthouse_98k_k1536_hbm_traffic.md"
 
 
@@ -83,8 +90,8 @@ def sources_sha256(paths):
 
 
 def symbol_group(symbol):
-    for syms, group in KERNEL_SYMBOLS.values():
-        if symbol in syms:
+    for name, (_, group) in KERNEL_SYMBOLS.items():
+        if any(symbol in form for form in kernel_forms(name)):
             return group
     if symbol in SCATTER_EXTRA:
         return "scatter"
@@ -100,7 +107,7 @@ def stored_traffic(kernel, workload="llama530m_98k_k1536"):
     another one, or the kernel's sources changed since."""
     if workload != "llama530m_98k_k1536" or kernel not in KERNEL_SYMBOLS:
         return None
-    symbols, group = KERNEL_SYMBOLS[kernel]
+    group = KERNEL_SYMBOLS[kernel][1]
     root = os.path.dirname(os.path.abspath(__file__))
     path = os.path.join(root, TRAFFIC_PROFILE)
     if not os.path.exists(path):
@@ -113,8 +120,11 @@ def stored_traffic(kernel, workload="llama530m_98k_k1536"):
                 fields[key.strip()] = val.strip().strip("`")
     if fields.get(f"sources_sha256.{group}") != sources_sha256(SOURCE_GROUPS[group]):
         return None
-    vals = [fields.get(f"hbm_bytes_per_launch.{sym}") for sym in symbols]
-    return sum(int(v) for v in vals) if all(v is not None for v in vals) else None
+    for form in kernel_forms(kernel):
+        vals = [fields.get(f"hbm_bytes_per_launch.{sym}") for sym in form]
+        if all(v is not None for v in vals):
+            return sum(int(v) for v in vals)
+    return None
 
 
 # the three instantiations of the projection GEMM, told apart by their operand / epilogue types
