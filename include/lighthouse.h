@@ -115,7 +115,10 @@ typedef struct {
 enum { LH_FWD_QG = 0, LH_FWD_KG, LH_FWD_VG, LH_FWD_QT, LH_FWD_KT, LH_FWD_VT, LH_FWD_O, LH_FWD_LSE };
 enum { LH_BWD_DO = 0, LH_BWD_DOT, LH_BWD_NEG_D, LH_BWD_DQ, LH_BWD_DK, LH_BWD_DV, LH_BWD_NEG_LSE };
 
-/* Host only; validates the descriptor and fills `out`.  No device work. */
+/* Host only; validates the descriptor and fills `out`.  No device work.
+ * LH_E_UNSUPPORTED also where one head's S rows (padded to 64) of d elements
+ * reach 2^32 bytes: the attention kernels address a head's rows with 32-bit
+ * byte offsets. */
 lh_status lh_make_plan(const lh_desc* desc, lh_plan* out);
 
 /* Stage 1, symmetric pyramid (skill card Stage 1; gist.science 2A).
@@ -171,7 +174,9 @@ lh_status lh_backward(const lh_desc* desc, const int32_t* gidx, const int32_t* g
  * with; equal to the layer at L = 1, skill card "selection-attention
  * decoupling").  o: out [B,H,N,d] dtype; lse: out [B,H,N] f32;
  * ws: out, dense_fwd_ws_bytes: the forward state (V transposed and the
- * output in f32), keep it for the backward.  p, L, k are not used. */
+ * output in f32), keep it for the backward.  p, L, k are not used.
+ * LH_E_UNSUPPORTED where one head's N rows (padded to 64) of d elements reach
+ * 2^32 bytes (32-bit row offsets in the kernels; the backward likewise). */
 lh_status dense_causal_attn(const lh_desc* desc, const void* q, const void* k, const void* v,
                             void* o, float* lse, void* ws, size_t ws_bytes, void* stream);
 

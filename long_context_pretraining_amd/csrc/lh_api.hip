@@ -22,6 +22,12 @@ inline size_t dense_transposed_bytes(const lh_desc* d) {
 
 bool aligned(const void* p) { return p && ((uintptr_t)p % 16) == 0; }
 
+// One head's padded sequence of rows fits 32-bit byte offsets (the attention
+// kernels' tile loads address a head's rows that way).
+bool rows_fit_u32(int64_t rows, const lh_desc* d) {
+    return round64(rows) * d->d * (int64_t)esize(d->dtype) < ((int64_t)1 << 32);
+}
+
 lh_status plan_impl(const lh_desc* d, lh_plan* out, LhGeom* g) {
     if (!d || !out) return LH_E_ARG;
     if (d->B < 1 || d->H < 1 || d->N < 1 || d->d < 1 || d->p < 2 || d->L < 1 || d->L > LH_MAX_LEVELS || d->k < 1)
@@ -60,6 +66,8 @@ lh_status plan_impl(const lh_desc* d, lh_plan* out, LhGeom* g) {
     P.S_formula = d->N / pw[d->L - 1] + (int64_t)(d->L - 1) * d->p * d->k;
     P.S_pad = round64(P.S);
     if (P.M_total >= ((int64_t)1 << 31)) return LH_E_UNSUPPORTED;
+    // the attention kernels address the S rows of one head with 32-bit byte offsets
+    if (!rows_fit_u32(P.S, d)) return LH_E_UNSUPPORTED;
 
     const int64_t BH = d->B * d->H, Mu = P.M_total - d->N;
     const size_t e = esize(d->dtype);
@@ -259,6 +267,7 @@ lh_status dense_causal_attn(const lh_desc* desc, const void* q, const void* k, c
     lh_plan P;
     lh_status s = plan_impl(desc, &P, nullptr);
     if (s != LH_OK) return s;
+    if (!rows_fit_u32(desc->N, desc)) return LH_E_UNSUPPORTED;   // the dense path attends over all N rows
     if (!aligned(q) || !aligned(k) || !aligned(v) || !aligned(o) || !aligned(lse) || !aligned(ws)) return LH_E_ARG;
     if (ws_bytes < P.dense_fwd_ws_bytes) return LH_E_WORKSPACE;
     hipStream_t st = (hipStream_t)stream;
@@ -283,6 +292,7 @@ lh_status dense_causal_attn_backward(const lh_desc* desc, const void* q, const v
     lh_plan P;
     lh_status s = plan_impl(desc, &P, nullptr);
     if (s != LH_OK) return s;
+    if (!rows_fit_u32(desc->N, desc)) return LH_E_UNSUPPORTED;   // the dense path attends over all N rows
     if (!aligned(q) || !aligned(k) || !aligned(v) || !aligned(fwd_ws) || !aligned(lse) || !aligned(dout) ||
         !aligned(dq) || !aligned(dk) || !aligned(dv) || !aligned(ws))
         return LH_E_ARG;

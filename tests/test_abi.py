@@ -62,6 +62,7 @@ def test_plan_golden_s():
     ((1, 1, 64, 96, 2, 2, 1, 1), lh.LH_E_UNSUPPORTED), # d = 96 not built
     ((1, 1, 64, 128, 2, 2, 1, 0), lh.LH_E_UNSUPPORTED),  # f32 with d = 128 not built
     ((1, 1, 8, 64, 4, 3, 1, 1), lh.LH_E_ARG),          # p^(L-1) > N
+    ((1, 1, 1 << 25, 64, 2, 1, 1, 1), lh.LH_E_UNSUPPORTED),  # L = 1: S = 2^25 rows of 128 B reach 2^32 bytes
 ])
 def test_plan_rejects(args, code):
     with pytest.raises(lh.LighthouseError) as e:
@@ -98,6 +99,22 @@ def test_entry_points_validate_before_launch():
     bad = lh.make_desc(1, 2, 4095, 64, 4, 3, 64, 1)
     assert _call("lh_forward", ctypes.byref(bad), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40, None) == lh.LH_E_ARG
     assert _call("lh_make_plan", None, None) == lh.LH_E_ARG
+
+
+def test_row_offset_limit():
+    """One head's rows must stay under 2^32 bytes (32-bit offsets in the
+    attention kernels): the last size below passes, the first at the limit is
+    refused, by the plan (sub-sequence S) and by the dense entry points (N)."""
+    below = lh.lh_make_plan(lh.make_desc(1, 1, (1 << 25) - 64, 64, 2, 1, 1, 1))
+    assert below.S == (1 << 25) - 64
+    # S small (L = 4), N = 2^25 bf16 rows of 128 B: the layer plans, the dense path refuses
+    desc = lh.make_desc(1, 1, 1 << 25, 64, 4, 4, 64, 1)
+    plan = lh.lh_make_plan(desc)
+    assert plan.S < (1 << 20)
+    D = ctypes.byref(desc)
+    assert _call("dense_causal_attn", D, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40, None) == lh.LH_E_UNSUPPORTED
+    assert _call("dense_causal_attn_backward", D, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                 1 << 40, None) == lh.LH_E_UNSUPPORTED
 
 
 def test_tensor_marshalling_rejects_host_tensors():
