@@ -196,19 +196,52 @@ __device__ __forceinline__ void stage_block_rows(const MapGeo& G, const int32_t*
     __syncthreads();
 }
 
-// x[l] = the 8 f32 elements vv*8 .. vv*8+7 of token t's level-l row (zeros
-// where the entry is not selected).
-template <int L, int D, int SHIFT>
-__device__ __forceinline__ void pull_token(const MapGeo& G, const float* rows_g, const int32_t* slot,
-                                           const float* rows, const int64_t* lo, const int* base, int64_t t, int vv,
-                                           floatx8* x) {
-    const int32_t g0 = slot[(int)(t - lo[0])];   // level 0: i_0(t) = t
-    x[0] = floatx8{};
-    if (g0 >= 0 && g0 < G.S) x[0] = *reinterpret_cast<const floatx8*>(rows_g + (int64_t)g0 * D + vv * 8);
+// Token loop of the pull kernels.  A task is the 8-element chunk vv of token
+// t (consecutive lanes on consecutive chunks, so a wave stores 1 KB runs);
+// emit(t, vv, x) gets x[l] = elements vv*8 .. vv*8+7 of token t's level-l row
+// (zeros where the entry is not selected).  A thread takes its tasks in pairs
+// and requests both level-0 rows (global memory, only where selected) before
+// it stores either result: stores and loads share one in-order completion
+// counter, so a wait for a load issued after a store also waits for that
+// store.  (Larger groups cost more registers than the waits they save:
+// these kernels live on occupancy.)
+template <int L, int D, int SHIFT, class Emit>
+__device__ __forceinline__ void pull_tokens(const MapGeo& G, const float* rows_g, const int32_t* slot,
+                                            const float* rows, const int64_t* lo, const int* base, int64_t t0,
+                                            int64_t t1, Emit&& emit) {
+    constexpr int NVEC = D / 8, C = 2;
+    const int ntask = (int)(t1 - t0 + 1) * NVEC;
+    const int s0 = (int)(t0 - lo[0]);
+    for (int first = threadIdx.x; first < ntask; first += C * kThreads) {
+        floatx8 x0[C];
 #pragma unroll
-    for (int l = 1; l < L; ++l) {
-        const int e = base[l] - base[1] + (int)((int64_t)div_pw(G, l, (uint32_t)(t + SHIFT)) - SHIFT - lo[l]);
-        x[l] = *reinterpret_cast<const floatx8*>(rows + e * D + vv * 8);
+        for (int c = 0; c < C; ++c) {
+            const int task = first + c * kThreads;
+            x0[c] = floatx8{};
+            if (task < ntask) {
+                const int tl = task / NVEC, vv = task - tl * NVEC;
+                const int32_t g0 = slot[s0 + tl];   // level 0: i_0(t) = t
+                if (g0 >= 0 && g0 < G.S)
+                    x0[c] = *reinterpret_cast<const floatx8*>(rows_g + (int64_t)g0 * D + vv * 8);
+            }
+        }
+#pragma unroll
+        for (int c = 0; c < C; ++c) {
+            const int task = first + c * kThreads;
+            if (task < ntask) {
+                const int tl = task / NVEC, vv = task - tl * NVEC;
+                const int64_t t = t0 + tl;
+                floatx8 x[L];
+                x[0] = x0[c];
+#pragma unroll
+                for (int l = 1; l < L; ++l) {
+                    const int e =
+                        base[l] - base[1] + (int)((int64_t)div_pw(G, l, (uint32_t)(t + SHIFT)) - SHIFT - lo[l]);
+                    x[l] = *reinterpret_cast<const floatx8*>(rows + e * D + vv * 8);
+                }
+                emit(t, vv, x);
+            }
+        }
     }
 }
 
@@ -222,7 +255,6 @@ __global__ __launch_bounds__(kThreads) void scatter_fwd_kernel(const float* __re
                                                                const int32_t* __restrict__ gpos,
                                                                T* __restrict__ o, MapGeo G, PullLds P) {
     typedef typename Frag<T>::type OV;
-    constexpr int NVEC = D / 8;
     extern __shared__ __align__(16) unsigned char smem[];
     float* rows = reinterpret_cast<float*>(smem);
     int32_t* slot = reinterpret_cast<int32_t*>(smem + (size_t)P.row_cap * D * 4);
@@ -232,12 +264,7 @@ __global__ __launch_bounds__(kThreads) void scatter_fwd_kernel(const float* __re
     int64_t lo[L];
     int base[L];
     stage_block_rows<L, D, 1>(G, gpos + bh * G.M_total, ogh, t0, t1, slot, rows, lo, base);
-    const int ntask = (int)(t1 - t0 + 1) * NVEC;
-    for (int task = threadIdx.x; task < ntask; task += kThreads) {
-        const int tl = task / NVEC, vv = task - tl * NVEC;
-        const int64_t t = t0 + tl;
-        floatx8 x[L];
-        pull_token<L, D, 1>(G, ogh, slot, rows, lo, base, t, vv, x);
+    pull_tokens<L, D, 1>(G, ogh, slot, rows, lo, base, t0, t1, [&](int64_t t, int vv, const floatx8* x) {
         floatx8 acc = x[0];
 #pragma unroll
         for (int l = 1; l < L; ++l) acc += x[l];
@@ -247,7 +274,7 @@ __global__ __launch_bounds__(kThreads) void scatter_fwd_kernel(const float* __re
         // the layer output is not read again by this layer: a non-temporal store
         // keeps it from displacing cached inputs (measured 0.03-0.04 ms per step)
         __builtin_nontemporal_store(out, reinterpret_cast<OV*>(o + (bh * G.N + t) * D + vv * 8));
-    }
+    });
 }
 
 // ---------------------------------------------------------------------------
@@ -361,7 +388,6 @@ __global__ __launch_bounds__(kThreads) void gpool_bwd_kernel(const float* __rest
                                                              const int32_t* __restrict__ gpos, T* o0, T* o1, T* o2,
                                                              MapGeo G, PullLds P) {
     typedef typename Frag<T>::type OV;
-    constexpr int NVEC = D / 8;
     extern __shared__ __align__(16) unsigned char smem[];
     float* rows = reinterpret_cast<float*>(smem);
     int32_t* slot = reinterpret_cast<int32_t*>(smem + (size_t)P.row_cap * D * 4);
@@ -373,12 +399,7 @@ __global__ __launch_bounds__(kThreads) void gpool_bwd_kernel(const float* __rest
     int64_t lo[L];
     int base[L];
     stage_block_rows<L, D, 0>(G, gpos + bh * G.M_total, dxg, t0, t1, slot, rows, lo, base);
-    const int ntask = (int)(t1 - t0 + 1) * NVEC;
-    for (int task = threadIdx.x; task < ntask; task += kThreads) {
-        const int tl = task / NVEC, vv = task - tl * NVEC;
-        const int64_t t = t0 + tl;
-        floatx8 x[L];
-        pull_token<L, D, 0>(G, dxg, slot, rows, lo, base, t, vv, x);
+    pull_tokens<L, D, 0>(G, dxg, slot, rows, lo, base, t0, t1, [&](int64_t t, int vv, const floatx8* x) {
         float acc[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[e] = 0.f;
@@ -390,7 +411,7 @@ __global__ __launch_bounds__(kThreads) void gpool_bwd_kernel(const float* __rest
 #pragma unroll
         for (int e = 0; e < 8; ++e) r[e] = static_cast<T>(acc[e]);
         __builtin_nontemporal_store(r, reinterpret_cast<OV*>(out + (bh * G.N + t) * D + vv * 8));   // final gradient, as above
-    }
+    });
 }
 
 // ---------------------------------------------------------------------------
