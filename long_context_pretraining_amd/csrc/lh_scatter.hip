@@ -12,6 +12,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kRows = 64;   // rows (slots or tokens) per block
+constexpr int kGatherTasks = 4;   // 16-byte gather tasks per thread: 64 rows of up to 256 bytes
 
 struct MapGeo {
     int64_t BH, N, d, S, S_pad, Mu, M_total;
@@ -98,19 +99,41 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(const T* __restrict__ 
     const int64_t bh = blockIdx.y, s0 = (int64_t)blockIdx.x * kRows;
     const int ld = (int)G.d + VEC;
     const int nvec = (int)(G.d / VEC);
-    for (int task = threadIdx.x; task < kRows * nvec; task += kThreads) {
-        const int sl = task / nvec, vv = task - sl * nvec;
-        const int64_t s = s0 + sl;
-        VT val = {};
-        const int64_t flat = s < G.S ? gidx[bh * G.S + s] : -1;
-        if (flat >= 0 && flat < G.M_total) {   // a map entry outside the pyramid gathers zeros
-            const T* src = flat < G.N ? src0 + (bh * G.N + flat) * G.d : srcp + (bh * G.Mu + flat - G.N) * G.d;
-            val = *reinterpret_cast<const VT*>(src + vv * VEC);
-            *reinterpret_cast<VT*>(rows + (bh * G.S + s) * G.d + vv * VEC) = val;
-        }
-        if (transposed)
+    const int ntask = kRows * nvec;
+    // A thread's tasks (at most kGatherTasks for the built row widths) go
+    // through in three passes -- every slot's map entry, every row, every
+    // store -- so no load is issued after a store (a wait for it would also
+    // wait for the store).
+    for (int first = threadIdx.x; first < ntask; first += kGatherTasks * kThreads) {
+        int64_t flat[kGatherTasks];
 #pragma unroll
-            for (int i = 0; i < VEC; ++i) tile[sl * ld + vv * VEC + i] = val[i];
+        for (int u = 0; u < kGatherTasks; ++u) {
+            const int task = first + u * kThreads;
+            const int64_t s = s0 + task / nvec;
+            flat[u] = task < ntask && s < G.S ? gidx[bh * G.S + s] : -1;
+        }
+        VT val[kGatherTasks];
+#pragma unroll
+        for (int u = 0; u < kGatherTasks; ++u) {
+            const int task = first + u * kThreads;
+            const int sl = task / nvec, vv = task - sl * nvec;
+            val[u] = VT{};
+            if (flat[u] >= 0 && flat[u] < G.M_total) {   // a map entry outside the pyramid gathers zeros
+                const T* src = flat[u] < G.N ? src0 + (bh * G.N + flat[u]) * G.d
+                                             : srcp + (bh * G.Mu + flat[u] - G.N) * G.d;
+                val[u] = *reinterpret_cast<const VT*>(src + vv * VEC);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kGatherTasks; ++u) {
+            const int task = first + u * kThreads;
+            const int sl = task / nvec, vv = task - sl * nvec;
+            const int64_t s = s0 + sl;
+            if (task < ntask && s < G.S) *reinterpret_cast<VT*>(rows + (bh * G.S + s) * G.d + vv * VEC) = val[u];
+            if (transposed && task < ntask)
+#pragma unroll
+                for (int i = 0; i < VEC; ++i) tile[sl * ld + vv * VEC + i] = val[u][i];
+        }
     }
     if (!transposed) return;
     __syncthreads();
