@@ -57,6 +57,9 @@ def test_plan_golden_s():
     ((1, 1, 64, 64, 2, 9, 1, 1), lh.LH_E_ARG),         # L > 8
     ((1, 1, 64, 64, 2, 2, 0, 1), lh.LH_E_ARG),         # k < 1
     ((0, 1, 64, 64, 2, 2, 1, 1), lh.LH_E_ARG),         # B < 1
+    ((1, 0, 64, 64, 2, 2, 1, 1), lh.LH_E_ARG),         # no heads
+    ((1, 1, 0, 64, 2, 2, 1, 1), lh.LH_E_ARG),          # empty sequence
+    ((1, 1, 64, 0, 2, 2, 1, 1), lh.LH_E_ARG),          # empty rows (d = 0)
     ((1, 1, 64, 64, 2, 2, 1, 7), lh.LH_E_ARG),         # unknown dtype
     ((1, 1, 64, 60, 2, 2, 1, 1), lh.LH_E_ARG),         # d not a multiple of 8
     ((1, 1, 64, 96, 2, 2, 1, 1), lh.LH_E_UNSUPPORTED), # d = 96 not built
@@ -143,7 +146,9 @@ def test_projection_plan_and_argument_checks():
     for bad, status in [((B, 100, Dm, H, d), lh.LH_E_UNSUPPORTED),    # N not a multiple of 64
                         ((B, N, 96, H, d), lh.LH_E_UNSUPPORTED),      # Dm not a multiple of 64
                         ((B, N, Dm, H, 96), lh.LH_E_UNSUPPORTED),     # d not built
-                        ((0, N, Dm, H, d), lh.LH_E_ARG)]:
+                        ((0, N, Dm, H, d), lh.LH_E_ARG),              # empty batch
+                        ((B, 0, Dm, H, d), lh.LH_E_ARG),              # empty sequence
+                        ((B, N, Dm, 0, d), lh.LH_E_ARG)]:             # no heads
         with pytest.raises(lh.LighthouseError) as e:
             lh.lh_qkv_plan(lh.make_proj_desc(*bad))
         assert e.value.status == status
