@@ -316,6 +316,12 @@ __device__ uint32_t block_excl_scan(uint32_t v, uint32_t* wsum, uint32_t* total)
     return res;
 }
 
+__device__ __forceinline__ uint32_t wave_sum(uint32_t x) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) x += (uint32_t)__shfl_xor((int)x, o, 64);
+    return x;
+}
+
 __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restrict__ sigma,
                                                             uint32_t* __restrict__ words,
                                                             int32_t* __restrict__ prefix, TopkP P) {
@@ -332,6 +338,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restr
     const int64_t nw = (M + 31) / 32;
     const int tid = threadIdx.x;
     const bool all = (int64_t)kk >= M;
+    constexpr int kB = 8;   // loads in flight per thread (per lane of a wave in the bitmap pass)
 
     uint32_t tau = 0, take = 0;
     if (!all) {
@@ -341,9 +348,17 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restr
             const uint32_t dmask = pass == 2 ? 0xFFu : 0xFFFu;
             for (int b = tid; b < 4096; b += kTopkThreads) hist[b] = 0;
             __syncthreads();
-            for (int64_t i = tid; i < M; i += kTopkThreads) {
-                const uint32_t u = sg[i];
-                if ((u & pmask) == pre) atomicAdd(&hist[(u >> shift) & dmask], 1u);
+            for (int64_t i0 = tid; i0 < M; i0 += (int64_t)kTopkThreads * kB) {   // kB loads in flight
+                uint32_t uu[kB];
+#pragma unroll
+                for (int j = 0; j < kB; ++j) {
+                    const int64_t i = i0 + (int64_t)j * kTopkThreads;
+                    uu[j] = i < M ? sg[i] : 0u;
+                }
+#pragma unroll
+                for (int j = 0; j < kB; ++j)
+                    if (i0 + (int64_t)j * kTopkThreads < M && (uu[j] & pmask) == pre)
+                        atomicAdd(&hist[(uu[j] >> shift) & dmask], 1u);
             }
             __syncthreads();
             const int g = kTopkThreads - 1 - tid;     // descending bins
@@ -375,41 +390,75 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restr
         take = remaining;
     }
 
-    uint32_t carry_tie = 0, carry_pc = 0;
-    for (int64_t w0 = 0; w0 < nw; w0 += kTopkThreads) {
-        const int64_t w = w0 + tid;
-        uint32_t gt = 0, eq = 0;
-        if (w < nw) {
-            for (int b = 0; b < 32; ++b) {
-                const int64_t i = w * 32 + b;
-                if (i < M) {
-                    const uint32_t u = sg[i];
-                    if (all || u > tau) gt |= 1u << b;
-                    else if (u == tau) eq |= 1u << b;
+    // Bitmap and word prefixes.  Wave j owns the entries [j per, (j+1) per) of
+    // the level (per a multiple of 64, so two whole words per 64 entries):
+    // it counts its entries above tau and equal to tau, one exchange gives every
+    // wave the ties and selected entries before its range, and it then walks
+    // its range 64 entries at a time -- coalesced reads, ballots for the bits,
+    // the ties taken in index order -- with running counts of its own.
+    const int lane = tid & 63, wid = tid >> 6;
+    constexpr int kWaves = kTopkThreads / 64;
+    const int64_t per = (M + 64 * kWaves - 1) / (64 * kWaves) * 64;
+    const int64_t c0 = wid * per, c1 = c0 + per < M ? c0 + per : M;
+    uint32_t n_gt = 0, n_eq = 0;
+    for (int64_t g0 = c0; g0 < c1; g0 += 64 * kB) {
+        uint32_t uu[kB];
+#pragma unroll
+        for (int j = 0; j < kB; ++j) {
+            const int64_t i = g0 + 64 * j + lane;
+            uu[j] = i < c1 ? sg[i] : 0u;
+        }
+#pragma unroll
+        for (int j = 0; j < kB; ++j) {
+            const bool in = g0 + 64 * j + lane < c1;
+            n_gt += (in && (all || uu[j] > tau)) ? 1u : 0u;
+            n_eq += (in && !all && uu[j] == tau) ? 1u : 0u;
+        }
+    }
+    n_gt = wave_sum(n_gt);
+    n_eq = wave_sum(n_eq);
+    if (lane == 0) {
+        hist[wid] = n_gt;
+        hist[kWaves + wid] = n_eq;
+    }
+    __syncthreads();
+    uint32_t carry_tie = 0, carry_pc = 0;   // ties and selected entries before this wave's range
+    for (int j = 0; j < wid; ++j) {
+        const uint32_t e = hist[kWaves + j];
+        const uint32_t e_sel = take > carry_tie ? (take - carry_tie < e ? take - carry_tie : e) : 0u;
+        carry_pc += hist[j] + e_sel;
+        carry_tie += e;
+    }
+    const uint64_t below = (1ull << lane) - 1ull;
+    for (int64_t g0 = c0; g0 < c1; g0 += 64 * kB) {
+        uint32_t uu[kB];
+#pragma unroll
+        for (int j = 0; j < kB; ++j) {
+            const int64_t i = g0 + 64 * j + lane;
+            uu[j] = i < c1 ? sg[i] : 0u;
+        }
+#pragma unroll
+        for (int j = 0; j < kB; ++j) {
+            const int64_t i0 = g0 + 64 * j;
+            if (i0 >= c1) break;
+            const bool in = i0 + lane < c1;
+            const bool gt = in && (all || uu[j] > tau);
+            const bool eq = in && !all && uu[j] == tau;
+            const uint64_t eqm = __ballot(eq);
+            const bool sel = gt || (eq && carry_tie + (uint32_t)__popcll(eqm & below) < take);
+            const uint64_t selm = __ballot(sel);
+            if (lane == 0) {
+                const int64_t w = i0 / 32;
+                W[w] = (uint32_t)selm;
+                PC[w] = (int32_t)carry_pc;
+                if (w + 1 < nw) {
+                    W[w + 1] = (uint32_t)(selm >> 32);
+                    PC[w + 1] = (int32_t)(carry_pc + (uint32_t)__popc((uint32_t)selm));
                 }
             }
+            carry_tie += (uint32_t)__popcll(eqm);
+            carry_pc += (uint32_t)__popcll(selm);
         }
-        uint32_t tot;
-        const uint32_t ex = block_excl_scan((uint32_t)__popc(eq), wsum, &tot);
-        uint32_t sel = gt;
-        const uint32_t base = carry_tie + ex;
-        if (take > base) {
-            uint32_t want = take - base, e = eq;
-            while (want && e) {
-                const uint32_t low = e & (0u - e);
-                sel |= low;
-                e ^= low;
-                --want;
-            }
-        }
-        carry_tie += tot;
-        uint32_t tot2;
-        const uint32_t ex2 = block_excl_scan((uint32_t)__popc(sel), wsum, &tot2);
-        if (w < nw) {
-            W[w] = sel;
-            PC[w] = (int32_t)(carry_pc + ex2);
-        }
-        carry_pc += tot2;
     }
 }
 
