@@ -479,53 +479,73 @@ struct MapP {
         woff[LH_MAX_LEVELS];
 };
 
-__device__ __forceinline__ bool t_bit(const uint32_t* W, int64_t y) { return (W[y >> 5] >> (y & 31)) & 1u; }
+// Entries per head stay below 2^31 (the plan refuses more), so the map works
+// in 32-bit indices; (i + 1) p^(l - l') < 2N fits as well.
+__device__ __forceinline__ bool t_bit(const uint32_t* W, uint32_t y) { return (W[y >> 5] >> (y & 31)) & 1u; }
 
-__device__ __forceinline__ int64_t sel_before(const MapP& P, const uint32_t* Wh, const int32_t* PCh, int lp,
-                                              int64_t x) {
+__device__ __forceinline__ uint32_t sel_before(const MapP& P, const uint32_t* Wh, const int32_t* PCh, int lp,
+                                               uint32_t x) {
     if (lp == P.L - 1) return x;
-    const int64_t y = x / P.p, r = x - y * P.p;
+    const uint32_t p = (uint32_t)P.p;
+    const uint32_t y = x / p, r = x - y * p;
     const uint32_t* W = Wh + P.woff[lp + 1];
     const int32_t* PC = PCh + P.woff[lp + 1];
-    const int64_t Mn = P.M[lp + 1];
-    int64_t c;
-    if (y >= Mn) {
-        c = P.k_eff[lp + 1];
+    uint32_t c;
+    if (y >= (uint32_t)P.M[lp + 1]) {
+        c = (uint32_t)P.k_eff[lp + 1];
     } else {
         const uint32_t m = (1u << (y & 31)) - 1u;
-        c = PC[y >> 5] + __popc(W[y >> 5] & m);
+        c = (uint32_t)PC[y >> 5] + (uint32_t)__popc(W[y >> 5] & m);
     }
-    c *= P.p;
-    if (r && y < Mn && t_bit(W, y)) c += r;
+    c *= p;
+    if (r && y < (uint32_t)P.M[lp + 1] && t_bit(W, y)) c += r;
     return c;
 }
+
+constexpr int kMapEnt = 4;   // pyramid entries per thread, kThreads apart (coalesced stores)
 
 __global__ __launch_bounds__(kThreads) void map_kernel(const uint32_t* __restrict__ words,
                                                        const int32_t* __restrict__ prefix,
                                                        int32_t* __restrict__ gidx, int32_t* __restrict__ gpos,
                                                        MapP P) {
-    const int64_t id = (int64_t)blockIdx.x * kThreads + threadIdx.x;
     const int64_t bh = blockIdx.y;
-    if (id >= P.M_total) return;
-    int l = 0;
-    while (id >= P.off[l + 1]) ++l;
-    const int64_t i = id - P.off[l];
     const uint32_t* Wh = words + bh * P.words_total;
     const int32_t* PCh = prefix + bh * P.words_total;
-    const bool sel = (l == P.L - 1) || t_bit(Wh + P.woff[l + 1], i / P.p);
-    if (!sel) {
-        gpos[bh * P.M_total + id] = -1;
-        return;
+    const uint32_t first = blockIdx.x * (uint32_t)(kThreads * kMapEnt) + threadIdx.x;
+    // every entry's level and selection bit first (their loads in flight together) ...
+    uint32_t ii[kMapEnt];
+    int lv[kMapEnt];
+    bool sel[kMapEnt];
+#pragma unroll
+    for (int e = 0; e < kMapEnt; ++e) {
+        const uint32_t id = first + e * kThreads;
+        int l = 0;
+        while (l < P.L - 1 && (int64_t)id >= P.off[l + 1]) ++l;
+        lv[e] = l;
+        ii[e] = id - (uint32_t)P.off[l];
+        sel[e] = (int64_t)id < P.M_total &&
+                 (l == P.L - 1 || t_bit(Wh + P.woff[l + 1], ii[e] / (uint32_t)P.p));
     }
-    int64_t pos = sel_before(P, Wh, PCh, l, i);
-    for (int lp = 0; lp < l; ++lp) pos += sel_before(P, Wh, PCh, lp, (i + 1) * P.pw[l - lp]);
-    for (int lp = l + 1; lp < P.L; ++lp) {
-        const int64_t n = P.pw[lp - l];
-        pos += sel_before(P, Wh, PCh, lp, (i + n) / n - 1);
+    // ... then the slots of the selected ones
+#pragma unroll
+    for (int e = 0; e < kMapEnt; ++e) {
+        const uint32_t id = first + e * kThreads;
+        if ((int64_t)id >= P.M_total) continue;
+        int64_t pos = -1;
+        if (sel[e]) {
+            const int l = lv[e];
+            const uint32_t i = ii[e];
+            uint32_t q = sel_before(P, Wh, PCh, l, i);
+            for (int lp = 0; lp < l; ++lp) q += sel_before(P, Wh, PCh, lp, (i + 1) * (uint32_t)P.pw[l - lp]);
+            for (int lp = l + 1; lp < P.L; ++lp) {
+                const uint32_t n = (uint32_t)P.pw[lp - l];
+                q += sel_before(P, Wh, PCh, lp, (i + n) / n - 1);
+            }
+            pos = q < (uint32_t)P.S ? (int64_t)q : -1;   // always in range for a consistent bitmap
+        }
+        gpos[bh * P.M_total + id] = (int32_t)pos;
+        if (pos >= 0) gidx[bh * P.S + pos] = (int32_t)id;
     }
-    if (pos < 0 || pos >= P.S) pos = -1;   // unreachable for a consistent bitmap; never write out of range
-    gpos[bh * P.M_total + id] = (int32_t)pos;
-    if (pos >= 0) gidx[bh * P.S + pos] = (int32_t)id;
 }
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -617,7 +637,7 @@ hipError_t launch_map(const LhGeom& g, const uint32_t* words, const int32_t* pre
         P.M[l] = g.M[l]; P.k_eff[l] = g.k_eff[l]; P.pw[l] = g.pw[l]; P.woff[l] = g.words_off[l];
     }
     for (int l = 0; l <= g.L; ++l) P.off[l] = g.off[l];
-    dim3 grid((unsigned)ceil_div(g.M_total, kThreads), (unsigned)g.BH);
+    dim3 grid((unsigned)ceil_div(g.M_total, (int64_t)kThreads * kMapEnt), (unsigned)g.BH);
     map_kernel<<<grid, kThreads, 0, st>>>(words, prefix, gidx, gpos, P);
     return hipGetLastError();
 }
