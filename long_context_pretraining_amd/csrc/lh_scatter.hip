@@ -697,8 +697,6 @@ __global__ __launch_bounds__(kThreads) void dense_prep_kernel(const T* __restric
     if (doT) store_transposed(tile, ld, d, doT + bh * d * S_pad, S_pad, s0);
 }
 
-inline unsigned blocks_for(int64_t n) { return (unsigned)((n + kRows - 1) / kRows); }
-
 template <typename T> size_t tile_bytes(int64_t d) { return sizeof(T) * kRows * (d + V16<T>::N); }
 
 }  // namespace
