@@ -83,6 +83,21 @@ def test_exact_ties_select_lower_index():
     compare_head(w, q, k, v, dout, r, 0, 1)
 
 
+def test_all_scores_tied_across_wave_ranges():
+    """Every Q and K row equal, so every score of every level ties: each level's
+    top-K must take its lowest k indices.  N = 16384, p = 4, L = 3, k = 700:
+    the top-K kernel splits level 2 (1024 entries) into 64-entry and level 1
+    (4096) into 256-entry ranges, one per wave, so the run of taken ties
+    crosses several range boundaries at both levels."""
+    w = W("all_tied_bf16", 1, 1, 16384, 64, "bf16", 4, 3, 700, 112, False)
+    q, k, v, dout = _data(w)
+    q[:] = q[:, :, :1, :].clone()
+    k[:] = k[:, :, :1, :].clone()
+    r = run_layer(w, q, k, v, dout)
+    compare_selection(w, q, k, r)
+    compare_head(w, q, k, v, dout, r, 0, 0)
+
+
 @pytest.mark.parametrize("dtype,N,d", [("f32", 256, 64), ("bf16", 1000, 64), ("bf16", 777, 128)])
 def test_dense_parity(dtype, N, d):
     """dense_causal_attn(+backward) vs the oracle at L = 1."""
