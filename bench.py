@@ -61,7 +61,8 @@ ATTN_SOURCES = SOURCE_GROUPS["attn"]
 # bench name -> the kernel symbols (as the profiles name them) its call launches, and their source
 # group; a call with several forms lists each form's symbols (the first form found in a profile counts)
 KERNEL_SYMBOLS = {
-    "pool": (("pool_kernel",), "select"), "score": (("score_kernel",), "select"),
+    # pooling also gives the token norms, in its own pass where its lanes do not hold whole rows
+    "pool": ((("pool_kernel",), ("pool_kernel", "norm_kernel")), "select"), "score": (("score_kernel",), "select"),
     "topk": (("topk_kernel",), "select"), "map": (("map_kernel",), "select"),
     "gather": (("gather_kernel",), "scatter"), "attn_fwd": (("attn_fwd_kernel",), "attn"),
     "scatter_fwd": (("scatter_fwd_kernel",), "scatter"),
@@ -251,8 +252,8 @@ def algorithmic_work(name, w, plan):
     if name == "attn_dq":           # dS K (the recomputed products are not counted)
         return "mfma", BH * 1 * 2 * d * pairs, "flop"
     table = {
-        "pool": 3 * N * d * e + 3 * Mu * d * e,
-        "score": 2 * N * d * e + Mu * 4,
+        "pool": 3 * N * d * e + 3 * Mu * d * e + 2 * N * 4,   # + the token norms of q and k
+        "score": 2 * N * 4 + Mu * 4,
         "gather": 2 * 3 * S * d * e + S * 4,
         "scatter_fwd": S * d * 4 + N * d * e + plan.M_total * 4,
         "scatter_bwd": N * d * e + S * d * e + S * d * 4 + S * 4,

@@ -8,8 +8,8 @@
  * summary at gist.science/paper/2605.06554):
  *
  *   lh_pyramid     Stage 1: mean-pool Q, K and V into L levels, factor p.
- *   lh_score_topk  Stage 2: l2-norm scores, max-pool inheritance, per-level
- *                  top-K, and the gather map of the selected entries.
+ *   lh_score_topk  Stage 2: l2-norm scores (from the norms lh_pyramid leaves),
+ *                  max-pool inheritance, per-level top-K, and the gather map.
  *   lh_forward     Stage 3 and 4: gather, dense causal attention on the S
  *                  entries, scatter-back over the ranges R(l, i).
  *   lh_backward    Gradient flow back through scatter, attention, gather and
@@ -126,7 +126,11 @@ lh_status lh_make_plan(const lh_desc* desc, lh_plan* out);
  * mean of p^l consecutive tokens), computed in f32 with the children summed
  * in index order, stored once rounded to the dtype.
  * pyr: out, [3][B,H,M_total-N,d] dtype (tensor Q, K, V; levels 1..L-1
- * concatenated, level l of a head at row level_off[l]-N); pyr_bytes given. */
+ * concatenated, level l of a head at row level_off[l]-N), followed (L > 1)
+ * by the token norms ||q_t||, ||k_t|| as [2][B,H,N] f32 (the order below,
+ * under lh_score_topk), which the scores start from: the pass that pools Q
+ * and K reads every row once for both.  pyr_bytes given (0 at L = 1: then
+ * nothing is written). */
 lh_status lh_pyramid(const lh_desc* desc, const void* q, const void* k, const void* v,
                      void* pyr, size_t pyr_bytes, void* stream);
 
@@ -139,10 +143,12 @@ lh_status lh_pyramid(const lh_desc* desc, const void* q, const void* k, const vo
  * selected and their p children at level l-1 are gathered; the coarsest level
  * is gathered whole.  Gathered order: ascending (last token of the span,
  * level).
+ * pyr:  in, the buffer lh_pyramid filled for the same q, k (its token norms
+ *       are read; may be NULL at L = 1, where nothing is scored).
  * gidx: out [B,H,S] int32, flat id of the entry in each slot.
  * gpos: out [B,H,M_total] int32, slot of each entry or -1.
  * ws:   scratch of sel_ws_bytes.  Inputs must be finite. */
-lh_status lh_score_topk(const lh_desc* desc, const void* q, const void* k,
+lh_status lh_score_topk(const lh_desc* desc, const void* pyr,
                         int32_t* gidx, int32_t* gpos, void* ws, size_t ws_bytes, void* stream);
 
 /* Stage 3 and 4 (skill card Stage 3-4; gist.science 2C).

@@ -22,6 +22,11 @@ inline size_t dense_transposed_bytes(const lh_desc* d) {
 
 bool aligned(const void* p) { return p && ((uintptr_t)p % 16) == 0; }
 
+// Bytes of the pooled levels in the lh_pyramid buffer; the token norms follow.
+size_t pyr_levels_bytes(int64_t BH, int64_t Mu, const lh_desc* d) {
+    return (size_t)3 * BH * Mu * d->d * esize(d->dtype);
+}
+
 // One head's padded sequence of rows fits 32-bit byte offsets (the attention
 // kernels' tile loads address a head's rows that way).
 bool rows_fit_u32(int64_t rows, const lh_desc* d) {
@@ -77,7 +82,8 @@ lh_status plan_impl(const lh_desc* d, lh_plan* out, LhGeom* g) {
     const size_t rowf = (size_t)BH * P.S * d->d * 4;         // [BH,S,d] f32
     const size_t vec = (size_t)BH * P.S * 4;                 // [BH,S] f32
 
-    P.pyr_bytes = (size_t)3 * BH * Mu * d->d * e;
+    // pooled levels of q, k, v, then (L > 1) the token norms ||q_t||, ||k_t|| that the scores start from
+    P.pyr_bytes = pyr_levels_bytes(BH, Mu, d) + (d->L > 1 ? (size_t)2 * BH * d->N * 4 : 0);
     P.sel_ws_bytes = align_up((size_t)BH * Mu * 4) + 2 * align_up((size_t)BH * words * 4);
     size_t o = 0;
     const size_t fwd_sizes[8] = {row, row, row, colT, colT, colT, rowf, vec};
@@ -153,16 +159,18 @@ lh_status lh_pyramid(const lh_desc* desc, const void* q, const void* k, const vo
     if (!aligned(pyr)) return LH_E_ARG;
     if (pyr_bytes < P.pyr_bytes) return LH_E_WORKSPACE;
     hipStream_t st = (hipStream_t)stream;
-    return dev(probed(LH_KERNEL_POOL, st, [&] { return launch_pool(g, desc->dtype, q, k, v, pyr, st); }));
+    float* norms = (float*)at(pyr, pyr_levels_bytes(g.BH, g.Mu, desc));
+    return dev(probed(LH_KERNEL_POOL, st, [&] { return launch_pool(g, desc->dtype, q, k, v, pyr, norms, st); }));
 }
 
-lh_status lh_score_topk(const lh_desc* desc, const void* q, const void* k, int32_t* gidx, int32_t* gpos, void* ws,
+lh_status lh_score_topk(const lh_desc* desc, const void* pyr, int32_t* gidx, int32_t* gpos, void* ws,
                         size_t ws_bytes, void* stream) {
     lh_plan P;
     LhGeom g;
     lh_status s = plan_impl(desc, &P, &g);
     if (s != LH_OK) return s;
-    if (!aligned(q) || !aligned(k) || !aligned(gidx) || !aligned(gpos)) return LH_E_ARG;
+    if (!aligned(gidx) || !aligned(gpos)) return LH_E_ARG;
+    if (P.pyr_bytes && !aligned(pyr)) return LH_E_ARG;
     if (P.sel_ws_bytes && !aligned(ws)) return LH_E_ARG;
     if (ws_bytes < P.sel_ws_bytes) return LH_E_WORKSPACE;
     hipStream_t st = (hipStream_t)stream;
@@ -170,7 +178,8 @@ lh_status lh_score_topk(const lh_desc* desc, const void* q, const void* k, int32
     const size_t sz_sigma = align_up((size_t)g.BH * g.Mu * 4), sz_w = align_up((size_t)g.BH * g.words_total * 4);
     uint32_t* words = (uint32_t*)at(ws, sz_sigma);
     int32_t* prefix = (int32_t*)at(ws, sz_sigma + sz_w);
-    hipError_t e = probed(LH_KERNEL_SCORE, st, [&] { return launch_scores(g, desc->dtype, q, k, sigma, st); });
+    const float* norms = P.pyr_bytes ? (const float*)at(pyr, pyr_levels_bytes(g.BH, g.Mu, desc)) : nullptr;
+    hipError_t e = probed(LH_KERNEL_SCORE, st, [&] { return launch_scores(g, norms, sigma, st); });
     if (e == hipSuccess) e = probed(LH_KERNEL_TOPK, st, [&] { return launch_topk(g, sigma, words, prefix, st); });
     if (e == hipSuccess)
         e = probed(LH_KERNEL_MAP, st, [&] { return launch_map(g, words, prefix, gidx, gpos, st); });

@@ -18,10 +18,12 @@ struct LhGeom {
 };
 
 // selection-side kernels (lh_select.hip)
+// Pyramid levels 1 .. L-1 of q, k, v into pyr, and the token norms ||q_t||,
+// ||k_t|| ([2][BH][N] f32) into norms.
 hipError_t launch_pool(const LhGeom& g, int dtype, const void* q, const void* k, const void* v, void* pyr,
-                       hipStream_t st);
-hipError_t launch_scores(const LhGeom& g, int dtype, const void* q, const void* k, float* sigma,
-                         hipStream_t st);
+                       float* norms, hipStream_t st);
+// Scores of levels >= 1 (max-pooled ||q|| + ||k||) from the token norms.
+hipError_t launch_scores(const LhGeom& g, const float* norms, float* sigma, hipStream_t st);
 hipError_t launch_topk(const LhGeom& g, const float* sigma, uint32_t* words, int32_t* prefix, hipStream_t st);
 hipError_t launch_map(const LhGeom& g, const uint32_t* words, const int32_t* prefix, int32_t* gidx,
                       int32_t* gpos, hipStream_t st);

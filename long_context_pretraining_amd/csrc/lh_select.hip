@@ -12,9 +12,6 @@
 namespace {
 
 constexpr int kThreads = 256;
-#ifndef SCORE_U
-#define SCORE_U 2
-#endif
 
 // ---------------------------------------------------------------------------
 // Pyramid: level l entry i = (sum of the p children of level l-1, index
@@ -30,17 +27,49 @@ constexpr int kThreads = 256;
 template <class V>
 __device__ __forceinline__ V load_stream(const V* p) { return __builtin_nontemporal_load(p); }
 
+// One lane's chunk of CW elements (as CW / VEC 16-byte vectors): squares
+// rounded to f32 and added left to right.
+template <typename T, int CW>
+__device__ __forceinline__ float sumsq_chunk(const typename V16<T>::type* v) {
+#pragma clang fp contract(off)
+    constexpr int VEC = V16<T>::N;
+    float a = 0.f;
+#pragma unroll
+    for (int j = 0; j < CW / VEC; ++j)
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) {
+            const float x = to_f(v[j][i]);
+            const float sq = x * x;
+            a = a + sq;
+        }
+    return a;
+}
+
+__device__ __forceinline__ float tree8(float a) {
+#pragma clang fp contract(off)
+    const float t = a + __shfl_xor(a, 4, 64);
+    const float u = t + __shfl_xor(t, 2, 64);
+    return u + __shfl_xor(u, 1, 64);
+}
+
 struct PoolP {
     int64_t N, d, BH, Mu;
     int p, L, chunk, DS, nslices, nv_log2;   // DS / VEC = 1 << nv_log2 vectors per row slice
     int sub;                      // tokens per level-1 pass: chunk, or a power of p >= p^2 dividing it
     int64_t offu[LH_MAX_LEVELS];  // row of level l inside a head's pyramid block
     int epc[LH_MAX_LEVELS];       // entries of level l per chunk (chunk / p^l)
+    // Token norms ||q_t||, ||k_t|| ([2][BH][N] f32), written by the q and k
+    // blocks when their lanes hold whole rows as the norm order needs them
+    // (8 lanes of d / 8 elements each), else null (norm_kernel writes them).
+    // part_off: LDS float offset of the pass's per-lane partial sums of squares.
+    float* norms;
+    int part_off;
 };
 
 template <typename T>
 __global__ __launch_bounds__(kThreads) void pool_kernel(const T* __restrict__ x0, const T* __restrict__ x1,
                                                         const T* __restrict__ x2, T* __restrict__ pyr, PoolP P) {
+#pragma clang fp contract(off)   // the squares of the norm partials are rounded before the add
     extern __shared__ float lds[];
     constexpr int VEC = V16<T>::N;
     typedef typename V16<T>::type VT;
@@ -89,13 +118,25 @@ __global__ __launch_bounds__(kThreads) void pool_kernel(const T* __restrict__ x0
                         if (cb + u < P.p)
                             v[j][u] = load_stream(reinterpret_cast<const VT*>(src[j] + (int64_t)(cb + u) * P.d));
                     }
+                // With the norms, lane vv also sums the squares of its elements
+                // [8 vv, 8 vv + 8) of each child row, left to right (norm order).
+                const bool nrm = P.norms && blockIdx.z < 2;   // uniform
 #pragma unroll
                 for (int u = 0; u < 4; ++u)
                     if (cb + u < P.p)
 #pragma unroll
-                        for (int j = 0; j < 2; ++j)
+                        for (int j = 0; j < 2; ++j) {
+                            float ss = 0.f;
 #pragma unroll
-                            for (int i = 0; i < VEC; ++i) acc[j][i] += to_f(v[j][u][i]);
+                            for (int i = 0; i < VEC; ++i) {
+                                const float xv = to_f(v[j][u][i]);
+                                acc[j][i] += xv;
+                                const float sq = xv * xv;
+                                ss = ss + sq;
+                            }
+                            if (nrm && task[j] < nt)
+                                lds[P.part_off + ((task[j] >> 3) * P.p + cb + u) * 8 + (task[j] & 7)] = ss;
+                        }
             }
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
@@ -114,6 +155,19 @@ __global__ __launch_bounds__(kThreads) void pool_kernel(const T* __restrict__ x0
                 }
                 *reinterpret_cast<VT*>(ph + (P.offu[1] + (int64_t)cidx * P.epc[1] + e1 + e) * P.d + dim0 + vv * VEC) = out;
             }
+        }
+        if (P.norms && blockIdx.z < 2) {
+            // ||x_t|| of the pass's tokens from the 8 partial sums (the tree of the
+            // norm order: (a_r + a_{r+4}), (t_r + t_{r+2}), (u_0 + u_1)), stored contiguously
+            __syncthreads();
+            const float* part = lds + P.part_off;
+            float* nout = P.norms + ((int64_t)blockIdx.z * P.BH + bh) * P.N + c0 + sc;
+            for (int t = threadIdx.x; t < n1 * P.p; t += kThreads) {
+                const float* a = part + t * 8;
+                const float t0 = a[0] + a[4], t1 = a[1] + a[5], t2 = a[2] + a[6], t3 = a[3] + a[7];
+                nout[t] = sqrtf((t0 + t2) + (t1 + t3));
+            }
+            __syncthreads();   // the partials are reused by the next pass
         }
         if (P.L <= 2) continue;
         __syncthreads();
@@ -179,11 +233,13 @@ __global__ __launch_bounds__(kThreads) void pool_kernel(const T* __restrict__ x0
 }
 
 // ---------------------------------------------------------------------------
-// Scores: s_t = sqrt(SS(q_t)) + sqrt(SS(k_t)), f32.  Eight lanes per token;
-// lane r sums the squares of elements [r*d/8, (r+1)*d/8) left to right (the
-// product is rounded before the add: no contraction), then the xor-4, xor-2,
-// xor-1 butterflies give (a_r + a_{r+4}), (t_r + t_{r+2}), (u_0 + u_1).
-// Levels >= 1 take the max over their children (exact).
+// Scores: s_t = ||q_t|| + ||k_t||, f32, with ||x|| = sqrt(SS(x)): eight lanes
+// per token; lane r sums the squares of elements [r*d/8, (r+1)*d/8) left to
+// right (the product is rounded before the add: no contraction), then the
+// xor-4, xor-2, xor-1 butterflies give (a_r + a_{r+4}), (t_r + t_{r+2}),
+// (u_0 + u_1).  The norms come from the pooling pass, which streams every q
+// and k row anyway (pool_kernel where its lanes hold rows that way,
+// norm_kernel otherwise); levels >= 1 take the max over their children (exact).
 // ---------------------------------------------------------------------------
 struct ScoreP {
     int64_t N, d, BH, Mu;
@@ -192,66 +248,48 @@ struct ScoreP {
     int epc[LH_MAX_LEVELS];   // entries of level l per chunk (chunk / p^l)
 };
 
-// One lane's chunk of CW elements (as CW / VEC 16-byte vectors): squares
-// rounded to f32 and added left to right.
-template <typename T, int CW>
-__device__ __forceinline__ float sumsq_chunk(const typename V16<T>::type* v) {
-#pragma clang fp contract(off)
-    constexpr int VEC = V16<T>::N;
-    float a = 0.f;
-#pragma unroll
-    for (int j = 0; j < CW / VEC; ++j)
-#pragma unroll
-        for (int i = 0; i < VEC; ++i) {
-            const float x = to_f(v[j][i]);
-            const float sq = x * x;
-            a = a + sq;
-        }
-    return a;
-}
-
-__device__ __forceinline__ float tree8(float a) {
-#pragma clang fp contract(off)
-    const float t = a + __shfl_xor(a, 4, 64);
-    const float u = t + __shfl_xor(t, 2, 64);
-    return u + __shfl_xor(u, 1, 64);
-}
-
-// Level-0 scores of one chunk of tokens, 8 lanes per token; every lane first
-// loads its q and k chunks of kScoreU tokens (tok, tok + 32, ...) so that
-// 2 kScoreU 16-byte loads per lane are in flight, then reduces them.
-constexpr int kScoreU = SCORE_U;
+// ||x_t|| of one chunk of tokens of q (blockIdx.z = 0) or k (1), 8 lanes per
+// token; every lane first loads its chunks of kScoreU tokens (tok, tok + 32,
+// ...) so that kScoreU 16-byte loads per lane are in flight.
+constexpr int kScoreU = 4;
 template <typename T, int D>
-__global__ __launch_bounds__(kThreads) void score_kernel(const T* __restrict__ q, const T* __restrict__ k,
-                                                         float* __restrict__ sigma, ScoreP P) {
+__global__ __launch_bounds__(kThreads) void norm_kernel(const T* __restrict__ q, const T* __restrict__ k,
+                                                        float* __restrict__ norms, ScoreP P) {
 #pragma clang fp contract(off)
-    extern __shared__ float lds[];
     typedef typename V16<T>::type VT;
     const int64_t bh = blockIdx.y;
     const int64_t c0 = (int64_t)blockIdx.x * P.chunk;
     const int len = (int)((P.N - c0) < P.chunk ? (P.N - c0) : P.chunk);
     constexpr int CW = D / 8, NV = CW / V16<T>::N, STEP = kThreads / 8;
     const int r = threadIdx.x & 7;
-    const T* qb = q + (bh * P.N + c0) * D + r * CW;
-    const T* kb = k + (bh * P.N + c0) * D + r * CW;
+    const T* xb = (blockIdx.z == 0 ? q : k) + (bh * P.N + c0) * D + r * CW;
+    float* nb = norms + ((int64_t)blockIdx.z * P.BH + bh) * P.N + c0;
     for (int tok0 = threadIdx.x >> 3; tok0 < len; tok0 += kScoreU * STEP) {
-        VT qv[kScoreU][NV], kv[kScoreU][NV];
+        VT xv[kScoreU][NV];
 #pragma unroll
         for (int u = 0; u < kScoreU; ++u) {
             const int tok = tok0 + u * STEP < len ? tok0 + u * STEP : tok0;   // tail: repeat a valid token
 #pragma unroll
-            for (int j = 0; j < NV; ++j) {
-                qv[u][j] = load_stream(reinterpret_cast<const VT*>(qb + (int64_t)tok * D) + j);
-                kv[u][j] = load_stream(reinterpret_cast<const VT*>(kb + (int64_t)tok * D) + j);
-            }
+            for (int j = 0; j < NV; ++j) xv[u][j] = load_stream(reinterpret_cast<const VT*>(xb + (int64_t)tok * D) + j);
         }
 #pragma unroll
         for (int u = 0; u < kScoreU; ++u) {
-            const float sq = tree8(sumsq_chunk<T, CW>(qv[u]));
-            const float sk = tree8(sumsq_chunk<T, CW>(kv[u]));
-            if (r == 0 && tok0 + u * STEP < len) lds[tok0 + u * STEP] = sqrtf(sq) + sqrtf(sk);
+            const float ss = tree8(sumsq_chunk<T, CW>(xv[u]));
+            if (r == 0 && tok0 + u * STEP < len) nb[tok0 + u * STEP] = sqrtf(ss);
         }
     }
+}
+
+__global__ __launch_bounds__(kThreads) void score_kernel(const float* __restrict__ norms,
+                                                         float* __restrict__ sigma, ScoreP P) {
+#pragma clang fp contract(off)
+    extern __shared__ float lds[];
+    const int64_t bh = blockIdx.y;
+    const int64_t c0 = (int64_t)blockIdx.x * P.chunk;
+    const int len = (int)((P.N - c0) < P.chunk ? (P.N - c0) : P.chunk);
+    const float* nq = norms + bh * P.N + c0;
+    const float* nk = norms + (P.BH + bh) * P.N + c0;
+    for (int t = threadIdx.x; t < len; t += kThreads) lds[t] = nq[t] + nk[t];
     __syncthreads();
     int prev_off = 0, cur_off = len;
     int n_prev = len;
@@ -553,8 +591,37 @@ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 }  // namespace
 
 // ---------------------------------------------------------------------------
+namespace {
+// Score geometry: chunks of a multiple of p^(L-1) tokens (at least 1024 where N allows).
+ScoreP score_params(const LhGeom& g) {
+    ScoreP P{};
+    P.N = g.N; P.d = g.d; P.BH = g.BH; P.Mu = g.Mu; P.p = g.p; P.L = g.L;
+    for (int l = 0; l < g.L; ++l) P.offu[l] = l ? g.off[l] - g.N : 0;
+    int64_t chunk = g.pw[g.L - 1];
+    while (chunk < 1024 && chunk * 2 <= g.N) chunk *= 2;
+    P.chunk = (int)chunk;
+    for (int l = 0; l < g.L; ++l) P.epc[l] = (int)(chunk / g.pw[l]);
+    return P;
+}
+
+// Token norms of q and k by their own pass (shapes the pooling pass does not cover).
+hipError_t launch_norms(const LhGeom& g, int dtype, const void* q, const void* k, float* norms, hipStream_t st) {
+    const ScoreP P = score_params(g);
+    dim3 grid((unsigned)ceil_div(g.N, P.chunk), (unsigned)g.BH, 2);
+    if (g.d != 64 && g.d != 128) return hipErrorInvalidValue;
+    if (dtype == LH_BF16) {
+        if (g.d == 64) norm_kernel<bf16, 64><<<grid, kThreads, 0, st>>>((const bf16*)q, (const bf16*)k, norms, P);
+        else norm_kernel<bf16, 128><<<grid, kThreads, 0, st>>>((const bf16*)q, (const bf16*)k, norms, P);
+    } else {
+        if (g.d == 64) norm_kernel<float, 64><<<grid, kThreads, 0, st>>>((const float*)q, (const float*)k, norms, P);
+        else norm_kernel<float, 128><<<grid, kThreads, 0, st>>>((const float*)q, (const float*)k, norms, P);
+    }
+    return hipGetLastError();
+}
+}  // namespace
+
 hipError_t launch_pool(const LhGeom& g, int dtype, const void* q, const void* k, const void* v, void* pyr,
-                       hipStream_t st) {
+                       float* norms, hipStream_t st) {
     if (g.L < 2) return hipSuccess;
     PoolP P{};
     P.N = g.N; P.d = g.d; P.BH = g.BH; P.Mu = g.Mu; P.p = g.p; P.L = g.L;
@@ -582,36 +649,31 @@ hipError_t launch_pool(const LhGeom& g, int dtype, const void* q, const void* k,
     while ((VEC << P.nv_log2) < DS) ++P.nv_log2;
     if ((VEC << P.nv_log2) != DS) return hipErrorInvalidValue;
     for (int l = 0; l < g.L; ++l) P.epc[l] = (int)(chunk / g.pw[l]);
-    dim3 grid((unsigned)(ceil_div(g.N, chunk) * P.nslices), (unsigned)g.BH, 3);
+    // the q and k blocks give the token norms when each of 8 lanes holds d / 8 elements of whole rows
+    // (8 partial sums per token of a pass in LDS)
     size_t sh = (size_t)lds_bytes(chunk, sub, DS);
+    const bool fused = P.nslices == 1 && DS == 8 * VEC && sh + (size_t)sub * 32 <= 64 * 1024;
+    P.norms = fused ? norms : nullptr;
+    P.part_off = (int)(sh / 4);
+    if (fused) sh += (size_t)sub * 32;
+    dim3 grid((unsigned)(ceil_div(g.N, chunk) * P.nslices), (unsigned)g.BH, 3);
     if (dtype == LH_BF16)
         pool_kernel<bf16><<<grid, kThreads, sh, st>>>((const bf16*)q, (const bf16*)k, (const bf16*)v, (bf16*)pyr, P);
     else
         pool_kernel<float><<<grid, kThreads, sh, st>>>((const float*)q, (const float*)k, (const float*)v, (float*)pyr, P);
-    return hipGetLastError();
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || fused) return e;
+    return launch_norms(g, dtype, q, k, norms, st);
 }
 
-hipError_t launch_scores(const LhGeom& g, int dtype, const void* q, const void* k, float* sigma, hipStream_t st) {
+hipError_t launch_scores(const LhGeom& g, const float* norms, float* sigma, hipStream_t st) {
     if (g.L < 2) return hipSuccess;
-    ScoreP P{};
-    P.N = g.N; P.d = g.d; P.BH = g.BH; P.Mu = g.Mu; P.p = g.p; P.L = g.L;
-    for (int l = 0; l < g.L; ++l) P.offu[l] = l ? g.off[l] - g.N : 0;
-    int64_t chunk = g.pw[g.L - 1];
-    while (chunk < 1024 && chunk * 2 <= g.N) chunk *= 2;
-    if (chunk > 16384) return hipErrorInvalidValue;
-    P.chunk = (int)chunk;
-    for (int l = 0; l < g.L; ++l) P.epc[l] = (int)(chunk / g.pw[l]);
-    int64_t ent = chunk;
-    for (int l = 1; l < g.L; ++l) ent += chunk / g.pw[l];
-    dim3 grid((unsigned)ceil_div(g.N, chunk), (unsigned)g.BH);
-    if (g.d != 64 && g.d != 128) return hipErrorInvalidValue;
-    if (dtype == LH_BF16) {
-        if (g.d == 64) score_kernel<bf16, 64><<<grid, kThreads, ent * 4, st>>>((const bf16*)q, (const bf16*)k, sigma, P);
-        else score_kernel<bf16, 128><<<grid, kThreads, ent * 4, st>>>((const bf16*)q, (const bf16*)k, sigma, P);
-    } else {
-        if (g.d == 64) score_kernel<float, 64><<<grid, kThreads, ent * 4, st>>>((const float*)q, (const float*)k, sigma, P);
-        else score_kernel<float, 128><<<grid, kThreads, ent * 4, st>>>((const float*)q, (const float*)k, sigma, P);
-    }
+    const ScoreP P = score_params(g);
+    if (P.chunk > 16384) return hipErrorInvalidValue;   // the chunk's levels in LDS
+    int64_t ent = P.chunk;
+    for (int l = 1; l < g.L; ++l) ent += P.chunk / g.pw[l];
+    dim3 grid((unsigned)ceil_div(g.N, P.chunk), (unsigned)g.BH);
+    score_kernel<<<grid, kThreads, ent * 4, st>>>(norms, sigma, P);
     return hipGetLastError();
 }
 

@@ -59,7 +59,7 @@ _SZ = ctypes.c_size_t
 _SIGS = {
     "lh_make_plan": [ctypes.POINTER(LhDesc), ctypes.POINTER(LhPlan)],
     "lh_pyramid": [ctypes.POINTER(LhDesc), _VP, _VP, _VP, _VP, _SZ, _VP],
-    "lh_score_topk": [ctypes.POINTER(LhDesc), _VP, _VP, _VP, _VP, _VP, _SZ, _VP],
+    "lh_score_topk": [ctypes.POINTER(LhDesc), _VP, _VP, _VP, _VP, _SZ, _VP],
     "lh_forward": [ctypes.POINTER(LhDesc), _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP],
     "lh_backward": [ctypes.POINTER(LhDesc), _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP],
     "dense_causal_attn": [ctypes.POINTER(LhDesc), _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP],
@@ -151,8 +151,8 @@ def lh_pyramid(desc, q, k, v, pyr, stream=None):
                                      _stream(stream)), "lh_pyramid")
 
 
-def lh_score_topk(desc, q, k, gidx, gpos, ws, stream=None):
-    _check(load_library().lh_score_topk(ctypes.byref(desc), _p(q), _p(k), _p(gidx), _p(gpos), _p(ws),
+def lh_score_topk(desc, pyr, gidx, gpos, ws, stream=None):
+    _check(load_library().lh_score_topk(ctypes.byref(desc), _p(pyr), _p(gidx), _p(gpos), _p(ws),
                                         _nbytes(ws), _stream(stream)), "lh_score_topk")
 
 
@@ -222,7 +222,7 @@ class LighthouseLayer:
         if self.pyr is not None:
             lh_pyramid(self.desc, q, k, v, self.pyr, stream)
         if select:
-            lh_score_topk(self.desc, q, k, self.gidx, self.gpos, self.sel_ws, stream)
+            lh_score_topk(self.desc, self.pyr, self.gidx, self.gpos, self.sel_ws, stream)
         lh_forward(self.desc, q, k, v, self.pyr, self.gidx, self.gpos, o, self.fwd_ws, stream)
 
     def backward(self, dout, dq, dk, dv, stream=None):

@@ -172,12 +172,16 @@ def _sumsq_f32(x: np.ndarray) -> np.ndarray:
     return u[:, 0] + u[:, 1]
 
 
+def token_norms(x: np.ndarray) -> np.ndarray:
+    """||x_t|| of every row in float32 (reading R2: the fixed chunked order,
+    then a correctly rounded float32 sqrt)."""
+    return np.sqrt(_sumsq_f32(x))
+
+
 def token_scores(q: np.ndarray, k: np.ndarray) -> np.ndarray:
     """Parameter-free score of every token: ||q_t|| + ||k_t|| in float32
     ([SK] Stage 2 names the two l2 norms; [GE] 2B; reading R1)."""
-    nq = np.sqrt(_sumsq_f32(q))            # float32 sqrt: correctly rounded
-    nk = np.sqrt(_sumsq_f32(k))
-    return (nq + nk).astype(np.float32)
+    return (token_norms(q) + token_norms(k)).astype(np.float32)
 
 
 def level_scores(s: np.ndarray, p: int, L: int) -> list:

@@ -67,7 +67,11 @@ def run_layer(w: inputs.Workload, q, k, v, dout, runs: int = 1) -> GpuResult:
     r.runs = outs
     B, H, S, d = w.B, w.H, layer.plan.S, w.d
     Mu = layer.plan.M_total - w.N
-    r.pyr = layer.pyr.view(3, B, H, Mu, d) if layer.pyr is not None else None
+    r.pyr = r.norms = None
+    if layer.pyr is not None:   # the pooled levels, then the token norms of q and k ([2][B,H,N] f32)
+        nlev = 3 * B * H * Mu * d
+        r.pyr = layer.pyr[:nlev].view(3, B, H, Mu, d)
+        r.norms = layer.pyr[nlev:].view(torch.float32).view(2, B, H, w.N)
     r.og = layer.fwd_view(lh.FWD_O, torch.float32, (B, H, S, d))
     r.lse = layer.fwd_view(lh.FWD_LSE, torch.float32, (B, H, S))
     r.qg = layer.fwd_view(lh.FWD_QG, dt, (B, H, S, d))
@@ -132,5 +136,11 @@ def compare_head(w, q, k, v, dout, r, b, h, scale=None, check_bwd=True):
                                                       if not n.startswith("pyramid")))
     if not lse_ok:
         fails.append(f"{tag}: lse")
+    if r.norms is not None:   # the token norms the scores start from: bit for bit (reading R2)
+        for zi, (z, x) in enumerate((("q", q), ("k", k))):
+            ref = orc.token_norms(head_np(x, b, h).astype(np.float32))
+            got = r.norms[zi, b, h].cpu().numpy()
+            if not np.array_equal(got, ref):
+                fails.append(f"{tag}: ||{z}_t|| differs from the oracle at {int(np.sum(got != ref))} tokens")
     assert not fails, "\n".join(fails)
     return st

@@ -39,7 +39,8 @@ def test_plan_matches_oracle(N, p, L, k, d, dt):
     assert plan.M_total == ref.M_total and plan.S == ref.S and plan.S_formula == ref.S_formula
     assert plan.S_pad % 64 == 0 and plan.S <= plan.S_pad < plan.S + 64
     e = 4 if dt == 0 else 2
-    assert plan.pyr_bytes == 3 * 2 * (ref.M_total - N) * d * e
+    # pooled levels of q, k, v (B=1, H=2), then the token norms of q and k in f32 (L > 1)
+    assert plan.pyr_bytes == 3 * 2 * (ref.M_total - N) * d * e + (2 * 2 * N * 4 if L > 1 else 0)
     offs = list(plan.fwd_off)
     assert offs == sorted(offs) and all(o % 256 == 0 for o in offs) and plan.fwd_ws_bytes > offs[-1]
 
@@ -84,7 +85,8 @@ def test_entry_points_validate_before_launch():
     D = ctypes.byref(desc)
     # null pointers
     assert _call("lh_pyramid", D, None, FAKE, FAKE, FAKE, plan.pyr_bytes, None) == lh.LH_E_ARG
-    assert _call("lh_score_topk", D, FAKE, FAKE, None, FAKE, FAKE, plan.sel_ws_bytes, None) == lh.LH_E_ARG
+    assert _call("lh_score_topk", D, FAKE, None, FAKE, FAKE, plan.sel_ws_bytes, None) == lh.LH_E_ARG
+    assert _call("lh_score_topk", D, None, FAKE, FAKE, FAKE, plan.sel_ws_bytes, None) == lh.LH_E_ARG   # no pyramid
     assert _call("lh_forward", D, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, plan.fwd_ws_bytes, None) == lh.LH_E_ARG
     assert _call("lh_backward", D, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, plan.bwd_ws_bytes, None) == lh.LH_E_ARG
     # misaligned pointers
@@ -92,7 +94,7 @@ def test_entry_points_validate_before_launch():
     assert _call("dense_causal_attn", D, FAKE, FAKE, FAKE, FAKE, FAKE + 4, FAKE, plan.dense_fwd_ws_bytes, None) == lh.LH_E_ARG
     # short workspaces
     assert _call("lh_pyramid", D, FAKE, FAKE, FAKE, FAKE, plan.pyr_bytes - 1, None) == lh.LH_E_WORKSPACE
-    assert _call("lh_score_topk", D, FAKE, FAKE, FAKE, FAKE, FAKE, plan.sel_ws_bytes - 1, None) == lh.LH_E_WORKSPACE
+    assert _call("lh_score_topk", D, FAKE, FAKE, FAKE, FAKE, plan.sel_ws_bytes - 1, None) == lh.LH_E_WORKSPACE
     assert _call("lh_forward", D, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, plan.fwd_ws_bytes - 1, None) == lh.LH_E_WORKSPACE
     assert _call("lh_backward", D, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, plan.bwd_ws_bytes - 1, None) == lh.LH_E_WORKSPACE
     assert _call("dense_causal_attn", D, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, plan.dense_fwd_ws_bytes - 1, None) == lh.LH_E_WORKSPACE
