@@ -6,6 +6,8 @@
 // All of these are bandwidth- or latency-bound; nothing here is a dense
 // contraction, so no matrix cores: coalesced 16-byte loads, LDS staging of the
 // coarser levels, and wave shuffles for the per-token reductions.
+#include <type_traits>
+
 #include "lh_device.h"
 #include "lh_internal.h"
 
@@ -59,14 +61,15 @@ struct PoolP {
     int64_t offu[LH_MAX_LEVELS];  // row of level l inside a head's pyramid block
     int epc[LH_MAX_LEVELS];       // entries of level l per chunk (chunk / p^l)
     // Token norms ||q_t||, ||k_t|| ([2][BH][N] f32), written by the q and k
-    // blocks when their lanes hold whole rows as the norm order needs them
-    // (8 lanes of d / 8 elements each), else null (norm_kernel writes them).
+    // blocks when their lanes hold whole rows in the norm order's chunks (8
+    // lanes of d / 8 elements, or 16 of d / 16), else null (norm_kernel).
     // part_off: LDS float offset of the pass's per-lane partial sums of squares.
     float* norms;
     int part_off;
 };
 
-template <typename T>
+// PAIRS: the token norms' chunks span two lanes (16 lanes per row).
+template <typename T, bool PAIRS>
 __global__ __launch_bounds__(kThreads) void pool_kernel(const T* __restrict__ x0, const T* __restrict__ x1,
                                                         const T* __restrict__ x2, T* __restrict__ pyr, PoolP P) {
 #pragma clang fp contract(off)   // the squares of the norm partials are rounded before the add
@@ -118,8 +121,10 @@ __global__ __launch_bounds__(kThreads) void pool_kernel(const T* __restrict__ x0
                         if (cb + u < P.p)
                             v[j][u] = load_stream(reinterpret_cast<const VT*>(src[j] + (int64_t)(cb + u) * P.d));
                     }
-                // With the norms, lane vv also sums the squares of its elements
-                // [8 vv, 8 vv + 8) of each child row, left to right (norm order).
+                // With the norms, lane vv also sums the squares of its VEC elements of
+                // each child row, left to right (norm order).  A norm chunk (d / 8
+                // elements) is one lane's VEC or, with 16 lanes per row, two lanes':
+                // the odd lane then continues from the even lane's sum.
                 const bool nrm = P.norms && blockIdx.z < 2;   // uniform
 #pragma unroll
                 for (int u = 0; u < 4; ++u)
@@ -134,8 +139,23 @@ __global__ __launch_bounds__(kThreads) void pool_kernel(const T* __restrict__ x0
                                 const float sq = xv * xv;
                                 ss = ss + sq;
                             }
-                            if (nrm && task[j] < nt)
-                                lds[P.part_off + ((task[j] >> 3) * P.p + cb + u) * 8 + (task[j] & 7)] = ss;
+                            if (!nrm) continue;
+                            int r = task[j] & nvm;
+                            if constexpr (PAIRS) {
+                                const float even = __shfl_xor(ss, 1, 64);
+                                if (r & 1) {
+                                    ss = even;
+#pragma unroll
+                                    for (int i = 0; i < VEC; ++i) {
+                                        const float xv = to_f(v[j][u][i]);
+                                        const float sq = xv * xv;
+                                        ss = ss + sq;
+                                    }
+                                }
+                                r = (r & 1) ? r >> 1 : -1;   // the odd lane holds the chunk's sum
+                            }
+                            if (r >= 0 && task[j] < nt)
+                                lds[P.part_off + ((task[j] >> P.nv_log2) * P.p + cb + u) * 8 + r] = ss;
                         }
             }
 #pragma unroll
@@ -649,18 +669,26 @@ hipError_t launch_pool(const LhGeom& g, int dtype, const void* q, const void* k,
     while ((VEC << P.nv_log2) < DS) ++P.nv_log2;
     if ((VEC << P.nv_log2) != DS) return hipErrorInvalidValue;
     for (int l = 0; l < g.L; ++l) P.epc[l] = (int)(chunk / g.pw[l]);
-    // the q and k blocks give the token norms when each of 8 lanes holds d / 8 elements of whole rows
-    // (8 partial sums per token of a pass in LDS)
+    // the q and k blocks give the token norms when whole rows are held by 8 lanes of d / 8 elements or
+    // 16 lanes of d / 16 (8 partial sums per token of a pass in LDS)
     size_t sh = (size_t)lds_bytes(chunk, sub, DS);
-    const bool fused = P.nslices == 1 && DS == 8 * VEC && sh + (size_t)sub * 32 <= 64 * 1024;
+    const bool fused = P.nslices == 1 && (DS == 8 * VEC || DS == 16 * VEC) && sh + (size_t)sub * 32 <= 64 * 1024;
     P.norms = fused ? norms : nullptr;
     P.part_off = (int)(sh / 4);
     if (fused) sh += (size_t)sub * 32;
     dim3 grid((unsigned)(ceil_div(g.N, chunk) * P.nslices), (unsigned)g.BH, 3);
-    if (dtype == LH_BF16)
-        pool_kernel<bf16><<<grid, kThreads, sh, st>>>((const bf16*)q, (const bf16*)k, (const bf16*)v, (bf16*)pyr, P);
-    else
-        pool_kernel<float><<<grid, kThreads, sh, st>>>((const float*)q, (const float*)k, (const float*)v, (float*)pyr, P);
+    auto launch = [&](auto kern, auto* x) {
+        typedef std::remove_const_t<std::remove_pointer_t<decltype(x)>> T;
+        kern<<<grid, kThreads, sh, st>>>((const T*)q, (const T*)k, (const T*)v, (T*)pyr, P);
+    };
+    const bool pairs = fused && DS == 16 * VEC;
+    if (dtype == LH_BF16) {
+        if (pairs) launch(pool_kernel<bf16, true>, (const bf16*)q);
+        else launch(pool_kernel<bf16, false>, (const bf16*)q);
+    } else {
+        if (pairs) launch(pool_kernel<float, true>, (const float*)q);
+        else launch(pool_kernel<float, false>, (const float*)q);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || fused) return e;
     return launch_norms(g, dtype, q, k, norms, st);
