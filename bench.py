@@ -341,8 +341,8 @@ def main():
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py runs on exactly one GPU: the layer is measured per GPU and this build has no "
-              "multi-GPU path (heads shard across GPUs with no communication; see the design notes).",
+        print("bench.py runs on exactly one GPU: the layer is measured per GPU and the library has no "
+              "multi-GPU path (heads would shard across GPUs with no communication).",
               file=sys.stderr)
         sys.exit(2)
 
@@ -413,7 +413,7 @@ def main():
                 "kernel_ms": round(dom_ms, 4), "work_per_launch": work}
 
     # every kernel of the step: its algorithmic rate against its roof and, where a counter
-    # summary of this build exists, the HBM bytes it actually moves
+    # summary of the current sources exists, the HBM bytes it actually moves
     stages = {}
     for name, ms in kernel_ms.items():
         b, wk, _ = algorithmic_work(name, w, plan)
