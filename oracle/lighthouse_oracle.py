@@ -26,8 +26,7 @@ exactly as a bf16/fp32 implementation stores it; the sub-sequence output
 itself is an intermediate and stays unrounded.  The "f64" dtype turns every
 rounding off (used by finite differences).
 
-Readings of points the pages leave open (each is used below and listed with
-its reasons in the design notes):
+Readings of points the pages leave open (each is used below):
   R1 score of an entry = ||q||_2 + ||k||_2 (the pages name both norms but not
      how they combine);
   R2 squared norm summed in float32 in a fixed order: 8 contiguous chunks of
