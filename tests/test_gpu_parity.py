@@ -98,6 +98,31 @@ def test_all_scores_tied_across_wave_ranges():
     compare_head(w, q, k, v, dout, r, 0, 0)
 
 
+def test_layer_on_a_side_stream():
+    """Every call enqueues on the stream it is given: the layer run on a side
+    stream (default priority), synchronised through that stream alone, gives
+    the default stream's results bit for bit."""
+    w = W("stream_bf16", 1, 2, 2048, 64, "bf16", 4, 3, 40, 113, True)
+    q, k, v, dout = _data(w)
+    dev = torch.device("cuda")
+
+    def run(stream):
+        layer = lh.LighthouseLayer(w.B, w.H, w.N, w.d, w.p, w.L, w.k, torch.bfloat16)
+        qd, kd, vd, dod = (t.to(dev) for t in (q, k, v, dout))
+        o, dq, dk, dv = (torch.empty_like(qd) for _ in range(4))
+        torch.cuda.synchronize()
+        layer.forward(qd, kd, vd, o, stream)
+        layer.backward(dod, dq, dk, dv, stream)
+        stream.synchronize()
+        return [t.cpu() for t in (o, dq, dk, dv, layer.gidx, layer.gpos)]
+
+    say("[stream] default vs side stream")
+    ref = run(torch.cuda.current_stream())
+    got = run(torch.cuda.Stream())
+    for name, a, b in zip(("o", "dq", "dk", "dv", "gidx", "gpos"), ref, got):
+        assert torch.equal(a, b), f"{name} differs on a side stream"
+
+
 @pytest.mark.parametrize("dtype,N,d", [("f32", 256, 64), ("bf16", 1000, 64), ("bf16", 777, 128)])
 def test_dense_parity(dtype, N, d):
     """dense_causal_attn(+backward) vs the oracle at L = 1."""
