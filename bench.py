@@ -328,8 +328,14 @@ def cpu_baseline(w, q, k, v, dout, nheads=6):
         orc.head_backward(st, gh)
         dt += time.perf_counter() - t0
     per_head = dt / nheads
+    cpu = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), cpu)
+    except OSError:
+        pass
     return {"value": round(w.B * w.N / (per_head * heads), 1), "unit": "tokens/s", "cores": int(cores),
-            "kind": "oracle",
+            "kind": "oracle", "cpu": cpu, "host_cpus": os.cpu_count(),
             "sample": f"{nheads} of {heads} heads (b=0, h<{nheads}), full fwd+bwd incl. selection, {dt:.1f} s "
                       f"of CPU time; value = B*N / (mean time per head x {heads} heads)"}
 
