@@ -360,12 +360,14 @@ __global__ __launch_bounds__(kThreads) void scatter_bwd_kernel(const T* __restri
 #pragma unroll
             for (int e = 0; e < VEC; ++e) acc[e] = 0.f;
             int t = 0;
-            for (; t + 4 <= len; t += 4) {   // four independent loads per step, summed in token order
-                VT x[4];
+            // eight independent loads per step (a 64-row range is 8 round trips, not 16),
+            // summed in token order
+            for (; t + 8 <= len; t += 8) {
+                VT x[8];
 #pragma unroll
-                for (int u = 0; u < 4; ++u) x[u] = *reinterpret_cast<const VT*>(src + (int64_t)(t + u) * G.d);
+                for (int u = 0; u < 8; ++u) x[u] = *reinterpret_cast<const VT*>(src + (int64_t)(t + u) * G.d);
 #pragma unroll
-                for (int u = 0; u < 4; ++u)
+                for (int u = 0; u < 8; ++u)
 #pragma unroll
                     for (int e = 0; e < VEC; ++e) acc[e] += to_f(x[u][e]);
             }
