@@ -58,6 +58,9 @@ from dataclasses import dataclass, field
 import numpy as np
 
 MAX_LEVELS = 8
+# Rows of the sub-sequence attention taken per group (memory only: each row is
+# computed whole, and the backward adds every group's dK, dV contributions).
+ATTN_ROW_BLOCK = 2048
 
 
 # --------------------------------------------------------------------------
@@ -261,7 +264,7 @@ def gather(levels: list, gidx: np.ndarray, plan: Plan) -> np.ndarray:
     return allrows[np.asarray(gidx, dtype=np.int64)]
 
 
-def attention_forward(Qt, Kt, Vt, scale: float, row_block: int = 2048):
+def attention_forward(Qt, Kt, Vt, scale: float, row_block: int = ATTN_ROW_BLOCK):
     """Causal softmax attention on the sub-sequence, float64.
 
     O_g = sum_{g' <= g} softmax_g'(scale q_g . k_g') v_g'; also returns the
@@ -283,7 +286,7 @@ def attention_forward(Qt, Kt, Vt, scale: float, row_block: int = 2048):
     return O, lse
 
 
-def attention_backward(Qt, Kt, Vt, Ot, dOt, lse, scale: float, row_block: int = 2048):
+def attention_backward(Qt, Kt, Vt, Ot, dOt, lse, scale: float, row_block: int = ATTN_ROW_BLOCK):
     """Gradients of causal attention w.r.t. its three inputs, float64.
 
     P is recomputed from the logits and the row log-sum-exp;
@@ -366,9 +369,10 @@ def gather_pool_backward(dXt: np.ndarray, gpos: np.ndarray, plan: Plan) -> np.nd
 # --------------------------------------------------------------------------
 # Whole layer, one head
 # --------------------------------------------------------------------------
-def head_forward(q, k, v, p, L, kk, dtype, scale=None, selection=None):
+def head_forward(q, k, v, p, L, kk, dtype, scale=None, selection=None, row_block=None):
     """Forward of one head.  q, k, v: [N, d] values of `dtype`.
-    `selection` = (gidx, gpos) freezes the selection (it is gradient-free)."""
+    `selection` = (gidx, gpos) freezes the selection (it is gradient-free);
+    `row_block` sets the attention's row groups (memory only)."""
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
@@ -383,10 +387,11 @@ def head_forward(q, k, v, p, L, kk, dtype, scale=None, selection=None):
         gidx, gpos = selection
     lq, lk, lv = pyramid(q, p, L, dtype), pyramid(k, p, L, dtype), pyramid(v, p, L, dtype)
     Qt, Kt, Vt = gather(lq, gidx, plan), gather(lk, gidx, plan), gather(lv, gidx, plan)
-    Ot, lse = attention_forward(Qt, Kt, Vt, scale)
+    rb = ATTN_ROW_BLOCK if row_block is None else row_block
+    Ot, lse = attention_forward(Qt, Kt, Vt, scale, rb)
     O = round_to(scatter(Ot, gpos, plan), dtype)
     return dict(plan=plan, scale=scale, gidx=gidx, gpos=gpos, levels=(lq, lk, lv),
-                Qt=Qt, Kt=Kt, Vt=Vt, Ot=Ot, lse=lse, O=O, dtype=dtype)
+                Qt=Qt, Kt=Kt, Vt=Vt, Ot=Ot, lse=lse, O=O, dtype=dtype, row_block=rb)
 
 def head_backward(st: dict, dO):
     """Backward of one head from the forward state and dO [N, d]."""
@@ -395,7 +400,7 @@ def head_backward(st: dict, dO):
     _check_finite(dO)
     dOt = round_to(scatter_backward(dO, st["gidx"], plan), dtype)
     dQt, dKt, dVt = attention_backward(st["Qt"], st["Kt"], st["Vt"], st["Ot"], dOt,
-                                       st["lse"], scale)
+                                       st["lse"], scale, st["row_block"])
     dq = round_to(gather_pool_backward(dQt, st["gpos"], plan), dtype)
     dk = round_to(gather_pool_backward(dKt, st["gpos"], plan), dtype)
     dv = round_to(gather_pool_backward(dVt, st["gpos"], plan), dtype)

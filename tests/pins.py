@@ -112,6 +112,22 @@ def check_gather_order(orc, q, k, plan):
             assert gpos[plan.level_off[l] + i] == pos
 
 
+def check_norm_order_golden(orc):
+    """Reading R2's summation order against hand-worked float32 sums of rows
+    whose result differs under other plausible orders (strided, sequential,
+    adjacent-pair tree); see tests/golden/norm_order.txt."""
+    for name, ones, r2, strided, seq, norm in read_golden("norm_order.txt"):
+        x = np.zeros((1, 64), dtype=np.float32)
+        x[0, 0] = 4096.0
+        for j in ones.split(","):
+            x[0, int(j)] = 1.0
+        got = orc._sumsq_f32(x)
+        assert got.dtype == np.float32
+        assert float(got[0]) == float(r2), (name, float(got[0]), r2)
+        assert float(r2) != float(strided) or float(r2) != float(seq)
+        assert float(orc.token_norms(x)[0]) == float(norm), (name, float(orc.token_norms(x)[0]), norm)
+
+
 # ---------------------------------------------------------------- scatter / causality
 def check_constant_v_fanin(orc, q, k, plan):
     """V rows all equal to c: every sub-sequence output equals c, so O_t is c
@@ -169,13 +185,14 @@ def check_causality_frozen(orc, q, k, v, plan, t, seed=4):
 
 
 # ---------------------------------------------------------------- attention
-def check_dense_vs_sdpa(orc, N=64, d=16, seed=5):
+def check_dense_vs_sdpa(orc, N=64, d=16, seed=5, row_block=None):
     """L = 1 is dense causal attention (skill card, selection-attention
     decoupling): compare with torch's scaled_dot_product_attention in
-    float64, forward and gradients."""
+    float64, forward and gradients.  A row_block below N runs the oracle's
+    attention in several row groups."""
     r = rng(seed)
     q, k, v, g = (r.standard_normal((N, d)) for _ in range(4))
-    st = orc.head_forward(q, k, v, 4, 1, 1, "f64")
+    st = orc.head_forward(q, k, v, 4, 1, 1, "f64", row_block=row_block)
     assert st["plan"].S == N and np.array_equal(st["gidx"], np.arange(N))
     tq, tk, tv = (torch.tensor(a, requires_grad=True) for a in (q, k, v))
     o = torch.nn.functional.scaled_dot_product_attention(tq[None, None], tk[None, None], tv[None, None],
@@ -188,19 +205,20 @@ def check_dense_vs_sdpa(orc, N=64, d=16, seed=5):
     np.testing.assert_allclose(bw["dv"], tv.grad.numpy(), rtol=1e-10, atol=1e-12)
 
 
-def check_finite_differences(orc, N, d, p, L, kk, seed, ncoord=24, h=1e-6):
+def check_finite_differences(orc, N, d, p, L, kk, seed, ncoord=24, h=1e-6, row_block=None):
     """Central differences of sum(O * G) with the selection frozen (the
     selection is gradient-free: skill card, gradient flow)."""
     r = rng(seed)
     q, k, v = (r.standard_normal((N, d)) * np.exp(0.5 * r.standard_normal((N, 1))) for _ in range(3))
     G = r.standard_normal((N, d))
-    st = orc.head_forward(q, k, v, p, L, kk, "f64")
+    st = orc.head_forward(q, k, v, p, L, kk, "f64", row_block=row_block)
     sel = (st["gidx"], st["gpos"])
     bw = orc.head_backward(st, G)
     grads = {"q": bw["dq"], "k": bw["dk"], "v": bw["dv"]}
 
     def loss(qq, kk_, vv):
-        return float(np.sum(orc.head_forward(qq, kk_, vv, p, L, kk, "f64", selection=sel)["O"] * G))
+        return float(np.sum(orc.head_forward(qq, kk_, vv, p, L, kk, "f64", selection=sel,
+                                             row_block=row_block)["O"] * G))
 
     for name in ("q", "k", "v"):
         gmax = np.abs(grads[name]).max()
@@ -213,3 +231,19 @@ def check_finite_differences(orc, N, d, p, L, kk, seed, ncoord=24, h=1e-6):
             lm = loss(args["q"], args["k"], args["v"])
             fd = (lp - lm) / (2 * h)
             assert abs(fd - grads[name][t, j]) <= 1e-6 * max(1.0, gmax), (name, t, j, fd, grads[name][t, j])
+
+
+def check_row_blocks(orc, S=100, d=16, seed=6, row_block=16):
+    """The attention's row groups bound memory only: groups of row_block < S
+    rows give the same output, log-sum-exp and gradients as one group."""
+    r = rng(seed)
+    Qt, Kt, Vt, dOt = (r.standard_normal((S, d)) * np.exp(0.5 * r.standard_normal((S, 1))) for _ in range(4))
+    scale = 1.0 / math.sqrt(d)
+    O1, lse1 = orc.attention_forward(Qt, Kt, Vt, scale, S)
+    O2, lse2 = orc.attention_forward(Qt, Kt, Vt, scale, row_block)
+    np.testing.assert_allclose(O2, O1, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(lse2, lse1, rtol=1e-12, atol=1e-12)
+    g1 = orc.attention_backward(Qt, Kt, Vt, O1, dOt, lse1, scale, S)
+    g2 = orc.attention_backward(Qt, Kt, Vt, O1, dOt, lse1, scale, row_block)
+    for a, b in zip(g2, g1):
+        np.testing.assert_allclose(a, b, rtol=1e-12, atol=1e-12 * np.abs(b).max())

@@ -110,6 +110,10 @@ def test_scores_golden_pythagorean():
     assert orc.token_scores(q64, k64)[0] == 12.0
 
 
+def test_norm_order_golden():
+    pins.check_norm_order_golden(orc)
+
+
 @pytest.mark.parametrize("d", [8, 64, 128])
 def test_scores_close_to_fp64_norms(d):
     r = pins.rng(d)
@@ -178,6 +182,15 @@ def test_dense_equals_sdpa():
     pins.check_dense_vs_sdpa(orc)
 
 
+def test_dense_equals_sdpa_in_row_groups():
+    # S = 100 rows in groups of 16: the last group is ragged (4 rows)
+    pins.check_dense_vs_sdpa(orc, N=100, row_block=16)
+
+
+def test_attention_row_groups_agree():
+    pins.check_row_blocks(orc)
+
+
 def test_zero_queries_give_running_mean():
     q, k, v = rand_qkv(256, 8, 12, "f64")
     q[:] = 0.0
@@ -229,6 +242,11 @@ def test_linear_in_values():
 def test_finite_differences(p, L, kk, seed):
     for h in range(2):
         pins.check_finite_differences(orc, 64, 8, p, L, kk, seed * 10 + h)
+
+
+def test_finite_differences_in_row_groups():
+    # S = 32 sub-sequence rows in groups of 8 (gradients summed over four groups)
+    pins.check_finite_differences(orc, 64, 8, 2, 3, 4, 77, row_block=8)
 
 
 def test_rejects_non_finite():

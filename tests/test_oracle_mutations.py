@@ -125,3 +125,54 @@ def test_unshifted_scatter_backward_fails_fd():
     m = fresh_oracle()
     m.scatter_ranges = lambda l, i, p, N: (i * p ** l, min(N - 1, (i + 1) * p ** l - 1))
     expect_failure(pins.check_finite_differences, m, 64, 8, 2, 3, 4, 1)
+
+
+def test_strided_norm_order_fails_golden():
+    m = fresh_oracle()
+
+    def sumsq(x):
+        x = np.asarray(x, dtype=np.float32)
+        a = np.zeros((x.shape[0], 8), dtype=np.float32)
+        for j in range(x.shape[1]):                     # element j into partial sum j mod 8
+            a[:, j % 8] = a[:, j % 8] + x[:, j] * x[:, j]
+        t = a[:, 0:4] + a[:, 4:8]
+        u = t[:, 0:2] + t[:, 2:4]
+        return u[:, 0] + u[:, 1]
+    m._sumsq_f32 = sumsq
+    expect_failure(pins.check_norm_order_golden, m)
+
+
+def test_sequential_norm_order_fails_golden():
+    m = fresh_oracle()
+
+    def sumsq(x):
+        x = np.asarray(x, dtype=np.float32)
+        a = np.zeros(x.shape[0], dtype=np.float32)
+        for j in range(x.shape[1]):
+            a = a + x[:, j] * x[:, j]
+        return a
+    m._sumsq_f32 = sumsq
+    expect_failure(pins.check_norm_order_golden, m)
+
+
+def test_overwritten_row_group_gradients_fail():
+    m = fresh_oracle()
+
+    def attention_backward(Qt, Kt, Vt, Ot, dOt, lse, scale, row_block=2048):
+        S, d = Qt.shape
+        dQ, dK, dV = np.zeros_like(Qt), np.zeros_like(Kt), np.zeros_like(Vt)
+        D = np.sum(dOt * Ot, axis=1)
+        for r0 in range(0, S, row_block):
+            r1 = min(S, r0 + row_block)
+            Z = scale * (Qt[r0:r1] @ Kt[:r1].T)
+            Z[np.arange(r1)[None, :] > np.arange(r0, r1)[:, None]] = -np.inf
+            P = np.exp(Z - lse[r0:r1, None])
+            dS = P * (dOt[r0:r1] @ Vt[:r1].T - D[r0:r1, None])
+            dQ[r0:r1] = scale * (dS @ Kt[:r1])
+            dK[:r1] = scale * (dS.T @ Qt[r0:r1])         # overwrites earlier groups' terms
+            dV[:r1] = P.T @ dOt[r0:r1]
+        return dQ, dK, dV
+    m.attention_backward = attention_backward
+    expect_failure(pins.check_row_blocks, m)
+    expect_failure(pins.check_dense_vs_sdpa, m, 100, 16, 5, 16)
+    expect_failure(pins.check_finite_differences, m, 64, 8, 2, 3, 4, 77, 24, 1e-6, 8)
