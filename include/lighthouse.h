@@ -8,8 +8,8 @@
  * summary at gist.science/paper/2605.06554):
  *
  *   lh_pyramid     Stage 1: mean-pool Q, K and V into L levels, factor p.
- *   lh_score_topk  Stage 2: l2-norm scores (from the norms lh_pyramid leaves),
- *                  max-pool inheritance, per-level top-K, and the gather map.
+ *   lh_score_topk  Stage 2: l2-norm scores of Q and K, max-pool inheritance,
+ *                  per-level top-K, and the gather map.
  *   lh_forward     Stage 3 and 4: gather, dense causal attention on the S
  *                  entries, scatter-back over the ranges R(l, i).
  *   lh_backward    Gradient flow back through scatter, attention, gather and
@@ -33,7 +33,9 @@
  *  - Results are deterministic: no atomics feed any output.
  *  - Supported on the GPU: dtype bf16 with d in {64, 128}, or f32 with
  *    d = 64; p >= 2; 1 <= L <= 8; k >= 1; N a multiple of p^(L-1);
- *    M_total < 2^31 (the maps are int32).
+ *    M_total < 2^31 (the maps are int32); p^(L-1) at most 16384 (the
+ *    pooling and score passes keep one chunk of that many tokens in LDS;
+ *    lh_make_plan returns LH_E_UNSUPPORTED above it).
  */
 #ifndef LIGHTHOUSE_H
 #define LIGHTHOUSE_H
@@ -128,9 +130,9 @@ lh_status lh_make_plan(const lh_desc* desc, lh_plan* out);
  * pyr: out, [3][B,H,M_total-N,d] dtype (tensor Q, K, V; levels 1..L-1
  * concatenated, level l of a head at row level_off[l]-N), followed (L > 1)
  * by the token norms ||q_t||, ||k_t|| as [2][B,H,N] f32 (the order below,
- * under lh_score_topk), which the scores start from: the pass that pools Q
- * and K reads every row once for both.  pyr_bytes given (0 at L = 1: then
- * nothing is written). */
+ * under lh_score_topk), which lh_score_topk may take instead of re-reading
+ * Q and K: the pass that pools Q and K reads every row once for both.
+ * pyr_bytes given (0 at L = 1: then nothing is written). */
 lh_status lh_pyramid(const lh_desc* desc, const void* q, const void* k, const void* v,
                      void* pyr, size_t pyr_bytes, void* stream);
 
@@ -143,12 +145,18 @@ lh_status lh_pyramid(const lh_desc* desc, const void* q, const void* k, const vo
  * selected and their p children at level l-1 are gathered; the coarsest level
  * is gathered whole.  Gathered order: ascending (last token of the span,
  * level).
- * pyr:  in, the buffer lh_pyramid filled for the same q, k (its token norms
- *       are read; may be NULL at L = 1, where nothing is scored).
+ * q, k: in [B,H,N,d] dtype, the layer's queries and keys.
+ * pyr:  optional (may be NULL).  NULL: the token norms are computed from q and
+ *       k (one more pass over both, into the end of ws).  Non-NULL: the buffer
+ *       lh_pyramid filled from these same q and k, earlier on this stream; its
+ *       token norms are used instead (bit-identical, and q and k are not read).
+ *       The library cannot tell a stale buffer from a current one: a pyramid
+ *       of other q, k gives the selection of those.
  * gidx: out [B,H,S] int32, flat id of the entry in each slot.
  * gpos: out [B,H,M_total] int32, slot of each entry or -1.
- * ws:   scratch of sel_ws_bytes.  Inputs must be finite. */
-lh_status lh_score_topk(const lh_desc* desc, const void* pyr,
+ * ws:   scratch of sel_ws_bytes; nothing in it needs clearing.  Inputs must
+ *       be finite. */
+lh_status lh_score_topk(const lh_desc* desc, const void* q, const void* k, const void* pyr,
                         int32_t* gidx, int32_t* gpos, void* ws, size_t ws_bytes, void* stream);
 
 /* Stage 3 and 4 (skill card Stage 3-4; gist.science 2C).
@@ -232,13 +240,14 @@ const char* lh_status_string(int status);
  * `kernel` records hipEvent_t `start` on its stream just before that launch
  * and `stop` just after it, so hipEventElapsedTime(start, stop) is the
  * kernel's duration as the stream sees it.  kernel = -1 (or null events)
- * switches the hook off.  The setting is process-wide and not thread-safe;
- * the events are owned by the caller. */
+ * switches the hook off.  The setting belongs to the calling thread: calls
+ * made from other threads never record the events, so concurrent callers on
+ * other threads are unaffected.  The events are owned by the caller. */
 enum {
     LH_KERNEL_POOL = 0, LH_KERNEL_SCORE, LH_KERNEL_TOPK, LH_KERNEL_MAP, LH_KERNEL_GATHER,
     LH_KERNEL_ATTN_FWD, LH_KERNEL_SCATTER_FWD, LH_KERNEL_SCATTER_BWD, LH_KERNEL_ATTN_DKDV,
     LH_KERNEL_ATTN_DQ, LH_KERNEL_GATHER_POOL_BWD, LH_KERNEL_TRANSPOSE, LH_KERNEL_DENSE_PREP,
-    LH_KERNEL_QKV_FWD, LH_KERNEL_QKV_BWD,
+    LH_KERNEL_QKV_FWD, LH_KERNEL_QKV_BWD, LH_KERNEL_NORM,
     LH_KERNEL_COUNT
 };
 lh_status lh_set_probe(int kernel, void* start_event, void* stop_event);

@@ -84,7 +84,10 @@ lh_status plan_impl(const lh_desc* d, lh_plan* out, LhGeom* g) {
 
     // pooled levels of q, k, v, then (L > 1) the token norms ||q_t||, ||k_t|| that the scores start from
     P.pyr_bytes = pyr_levels_bytes(BH, Mu, d) + (d->L > 1 ? (size_t)2 * BH * d->N * 4 : 0);
-    P.sel_ws_bytes = align_up((size_t)BH * Mu * 4) + 2 * align_up((size_t)BH * words * 4);
+    // level scores, top-K bitmaps and their prefixes, then (L > 1) room for the token norms when they
+    // are computed from q and k rather than taken from the pyramid buffer
+    P.sel_ws_bytes = align_up((size_t)BH * Mu * 4) + 2 * align_up((size_t)BH * words * 4) +
+                     (d->L > 1 ? align_up((size_t)2 * BH * d->N * 4) : 0);
     size_t o = 0;
     const size_t fwd_sizes[8] = {row, row, row, colT, colT, colT, rowf, vec};
     for (int i = 0; i < 8; ++i) { P.fwd_off[i] = o; o += align_up(fwd_sizes[i]); }
@@ -97,15 +100,15 @@ lh_status plan_impl(const lh_desc* d, lh_plan* out, LhGeom* g) {
     P.dense_fwd_ws_bytes = dT + align_up((size_t)BH * d->N * d->d * 4);
     P.dense_bwd_ws_bytes = 3 * dT + 2 * align_up((size_t)BH * d->N * 4);
 
+    G.BH = BH; G.N = d->N; G.d = d->d; G.S = P.S; G.S_pad = P.S_pad; G.M_total = P.M_total; G.Mu = Mu;
+    G.p = d->p; G.L = d->L;
+    for (int l = 0; l < d->L; ++l) { G.M[l] = P.M[l]; G.k_eff[l] = P.k_eff[l]; }
+    for (int l = 0; l <= d->L; ++l) G.off[l] = P.level_off[l];
+    G.words_total = words;
+    // the pooling and score passes keep a chunk's levels in LDS: refuse shapes without a layout that fits
+    if (!pool_fits(G, d->dtype) || !scores_fit(G)) return LH_E_UNSUPPORTED;
     *out = P;
-    if (g) {
-        G.BH = BH; G.N = d->N; G.d = d->d; G.S = P.S; G.S_pad = P.S_pad; G.M_total = P.M_total; G.Mu = Mu;
-        G.p = d->p; G.L = d->L;
-        for (int l = 0; l < d->L; ++l) { G.M[l] = P.M[l]; G.k_eff[l] = P.k_eff[l]; }
-        for (int l = 0; l <= d->L; ++l) G.off[l] = P.level_off[l];
-        G.words_total = words;
-        *g = G;
-    }
+    if (g) *g = G;
     return LH_OK;
 }
 
@@ -115,9 +118,11 @@ inline const unsigned char* at(const void* base, size_t off) { return static_cas
 
 float softmax_scale(const lh_desc* d) { return d->scale > 0.f ? d->scale : 1.0f / sqrtf((float)d->d); }
 
-// Measurement hook (lh_set_probe): events recorded around one kernel's launches.
-int g_probe_kernel = -1;
-hipEvent_t g_probe_start = nullptr, g_probe_stop = nullptr;
+// Measurement hook (lh_set_probe): events recorded around one kernel's
+// launches.  The setting belongs to the thread that made it, so calls from
+// other threads never see it.
+thread_local int g_probe_kernel = -1;
+thread_local hipEvent_t g_probe_start = nullptr, g_probe_stop = nullptr;
 
 template <class F>
 hipError_t probed(int id, hipStream_t st, F&& launch) {
@@ -163,27 +168,47 @@ lh_status lh_pyramid(const lh_desc* desc, const void* q, const void* k, const vo
     return dev(probed(LH_KERNEL_POOL, st, [&] { return launch_pool(g, desc->dtype, q, k, v, pyr, norms, st); }));
 }
 
-lh_status lh_score_topk(const lh_desc* desc, const void* pyr, int32_t* gidx, int32_t* gpos, void* ws,
-                        size_t ws_bytes, void* stream) {
-    lh_plan P;
-    LhGeom g;
-    lh_status s = plan_impl(desc, &P, &g);
-    if (s != LH_OK) return s;
-    if (!aligned(gidx) || !aligned(gpos)) return LH_E_ARG;
-    if (P.pyr_bytes && !aligned(pyr)) return LH_E_ARG;
-    if (P.sel_ws_bytes && !aligned(ws)) return LH_E_ARG;
-    if (ws_bytes < P.sel_ws_bytes) return LH_E_WORKSPACE;
-    hipStream_t st = (hipStream_t)stream;
+namespace {
+// Scores, top-K and the gather map into the selection workspace ws (laid out
+// as lh_make_plan sizes it).  The token norms come from pyr when it is given,
+// else from q and k by their own pass into the end of ws.
+hipError_t score_topk_impl(const LhGeom& g, const lh_desc* desc, const lh_plan& P, const void* q, const void* k,
+                           const void* pyr, int32_t* gidx, int32_t* gpos, void* ws, hipStream_t st) {
     float* sigma = (float*)ws;
     const size_t sz_sigma = align_up((size_t)g.BH * g.Mu * 4), sz_w = align_up((size_t)g.BH * g.words_total * 4);
     uint32_t* words = (uint32_t*)at(ws, sz_sigma);
     int32_t* prefix = (int32_t*)at(ws, sz_sigma + sz_w);
-    const float* norms = P.pyr_bytes ? (const float*)at(pyr, pyr_levels_bytes(g.BH, g.Mu, desc)) : nullptr;
-    hipError_t e = probed(LH_KERNEL_SCORE, st, [&] { return launch_scores(g, norms, sigma, st); });
+    hipError_t e = hipSuccess;
+    const float* norms = nullptr;
+    if (g.L > 1) {
+        if (pyr) {
+            norms = (const float*)at(pyr, pyr_levels_bytes(g.BH, g.Mu, desc));
+        } else {
+            float* own = (float*)at(ws, sz_sigma + 2 * sz_w);
+            e = probed(LH_KERNEL_NORM, st, [&] { return launch_norms(g, desc->dtype, q, k, own, st); });
+            norms = own;
+        }
+    }
+    if (e == hipSuccess) e = probed(LH_KERNEL_SCORE, st, [&] { return launch_scores(g, norms, sigma, st); });
     if (e == hipSuccess) e = probed(LH_KERNEL_TOPK, st, [&] { return launch_topk(g, sigma, words, prefix, st); });
     if (e == hipSuccess)
         e = probed(LH_KERNEL_MAP, st, [&] { return launch_map(g, words, prefix, gidx, gpos, st); });
-    return dev(e);
+    (void)P;
+    return e;
+}
+}  // namespace
+
+lh_status lh_score_topk(const lh_desc* desc, const void* q, const void* k, const void* pyr, int32_t* gidx,
+                        int32_t* gpos, void* ws, size_t ws_bytes, void* stream) {
+    lh_plan P;
+    LhGeom g;
+    lh_status s = plan_impl(desc, &P, &g);
+    if (s != LH_OK) return s;
+    if (!aligned(q) || !aligned(k) || !aligned(gidx) || !aligned(gpos)) return LH_E_ARG;
+    if (pyr && !aligned(pyr)) return LH_E_ARG;
+    if (P.sel_ws_bytes && !aligned(ws)) return LH_E_ARG;
+    if (ws_bytes < P.sel_ws_bytes) return LH_E_WORKSPACE;
+    return dev(score_topk_impl(g, desc, P, q, k, pyr, gidx, gpos, ws, (hipStream_t)stream));
 }
 
 lh_status lh_forward(const lh_desc* desc, const void* q, const void* k, const void* v, const void* pyr,

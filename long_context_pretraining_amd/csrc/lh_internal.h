@@ -22,6 +22,12 @@ struct LhGeom {
 // ||k_t|| ([2][BH][N] f32) into norms.
 hipError_t launch_pool(const LhGeom& g, int dtype, const void* q, const void* k, const void* v, void* pyr,
                        float* norms, hipStream_t st);
+// Token norms ||q_t||, ||k_t|| ([2][BH][N] f32) straight from q and k.
+hipError_t launch_norms(const LhGeom& g, int dtype, const void* q, const void* k, float* norms, hipStream_t st);
+// Whether the pooling and score passes have an LDS layout for this shape
+// (checked on the host before any launch).
+bool pool_fits(const LhGeom& g, int dtype);
+bool scores_fit(const LhGeom& g);
 // Scores of levels >= 1 (max-pooled ||q|| + ||k||) from the token norms.
 hipError_t launch_scores(const LhGeom& g, const float* norms, float* sigma, hipStream_t st);
 hipError_t launch_topk(const LhGeom& g, const float* sigma, uint32_t* words, int32_t* prefix, hipStream_t st);

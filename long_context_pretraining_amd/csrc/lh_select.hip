@@ -624,8 +624,55 @@ ScoreP score_params(const LhGeom& g) {
     return P;
 }
 
-// Token norms of q and k by their own pass (shapes the pooling pass does not cover).
+// Pooling geometry: a chunk of tokens (a multiple of p^(L-1)), taken in
+// passes of `sub` tokens, over row slices of DS elements, so that the f32
+// levels fit the LDS.  False where no such split fits.
+struct PoolShape {
+    int64_t chunk, sub, lds;
+    int DS;
+};
+constexpr int64_t kPoolLds = 48 * 1024;   // a few blocks per CU
+bool pool_shape(const LhGeom& g, int dtype, PoolShape* out) {
+    const int VEC = dtype == LH_BF16 ? 8 : 4;
+    int64_t chunk = g.pw[g.L - 1];
+    while (chunk < 256 && chunk * 2 <= g.N) chunk *= 2;
+    // chunk must stay a multiple of p^(L-1): it is p^(L-1) * 2^j
+    int DS = (int)g.d;
+    // f32 LDS: one pass's level 1 (sub / p entries) plus the chunk's levels 2 .. L-1
+    auto lds_bytes = [&](int64_t ch, int64_t sub, int ds) {
+        int64_t ent = sub / g.p;
+        for (int l = 2; l < g.L; ++l) ent += ch / g.pw[l];
+        return ent * ds * 4;
+    };
+    while (lds_bytes(chunk, chunk, DS) > kPoolLds && chunk > g.pw[g.L - 1]) chunk /= 2;
+    // whole rows in passes of p^j tokens (j >= 2, dividing p^(L-1) and so the
+    // chunk); where no pass fits whole rows, slice the rows of one pass over the
+    // chunk, or, where even the narrowest slice of that does not fit, of the
+    // smallest pass
+    int64_t sub = chunk;
+    for (int j = g.L - 2; j >= 2 && lds_bytes(chunk, sub, DS) > kPoolLds; --j) sub = g.pw[j];
+    if (lds_bytes(chunk, sub, DS) > kPoolLds && lds_bytes(chunk, chunk, VEC) <= kPoolLds) sub = chunk;
+    while (lds_bytes(chunk, sub, DS) > kPoolLds && DS > VEC) DS /= 2;
+    const int64_t lds = lds_bytes(chunk, sub, DS);
+    if (lds > 64 * 1024 || chunk > INT32_MAX) return false;
+    *out = PoolShape{chunk, sub, lds, DS};
+    return true;
+}
+
+// The score pass keeps one chunk's levels in LDS (f32).
+constexpr int64_t kScoreMaxChunk = 16384;
+}  // namespace
+
+bool pool_fits(const LhGeom& g, int dtype) {
+    PoolShape s;
+    return g.L < 2 || pool_shape(g, dtype, &s);
+}
+bool scores_fit(const LhGeom& g) { return g.L < 2 || score_params(g).chunk <= kScoreMaxChunk; }
+
+// Token norms of q and k by their own pass (shapes the pooling pass does not
+// cover, and scoring straight from q and k).
 hipError_t launch_norms(const LhGeom& g, int dtype, const void* q, const void* k, float* norms, hipStream_t st) {
+    if (g.L < 2) return hipSuccess;
     const ScoreP P = score_params(g);
     dim3 grid((unsigned)ceil_div(g.N, P.chunk), (unsigned)g.BH, 2);
     if (g.d != 64 && g.d != 128) return hipErrorInvalidValue;
@@ -638,7 +685,6 @@ hipError_t launch_norms(const LhGeom& g, int dtype, const void* q, const void* k
     }
     return hipGetLastError();
 }
-}  // namespace
 
 hipError_t launch_pool(const LhGeom& g, int dtype, const void* q, const void* k, const void* v, void* pyr,
                        float* norms, hipStream_t st) {
@@ -647,31 +693,17 @@ hipError_t launch_pool(const LhGeom& g, int dtype, const void* q, const void* k,
     P.N = g.N; P.d = g.d; P.BH = g.BH; P.Mu = g.Mu; P.p = g.p; P.L = g.L;
     for (int l = 0; l < g.L; ++l) P.offu[l] = l ? g.off[l] - g.N : 0;
     const int VEC = dtype == LH_BF16 ? 8 : 4;
-    int64_t chunk = g.pw[g.L - 1];
-    while (chunk < 256 && chunk * 2 <= g.N) chunk *= 2;
-    // chunk must stay a multiple of p^(L-1): it is p^(L-1) * 2^j
-    int DS = (int)g.d;
-    // f32 LDS: one pass's level 1 (sub / p entries) plus the chunk's levels 2 .. L-1
-    auto lds_bytes = [&](int64_t ch, int64_t sub, int ds) {
-        int64_t ent = sub / g.p;
-        for (int l = 2; l < g.L; ++l) ent += ch / g.pw[l];
-        return ent * ds * 4;
-    };
-    constexpr int64_t kPoolLds = 48 * 1024;   // a few blocks per CU
-    while (lds_bytes(chunk, chunk, DS) > kPoolLds && chunk > g.pw[g.L - 1]) chunk /= 2;
-    // whole rows in passes of p^j tokens (j >= 2, dividing p^(L-1) and so the chunk) before slicing rows
-    int64_t sub = chunk;
-    for (int j = g.L - 2; j >= 2 && lds_bytes(chunk, sub, DS) > kPoolLds; --j) sub = g.pw[j];
-    if (lds_bytes(chunk, sub, DS) > kPoolLds) sub = chunk;
-    while (lds_bytes(chunk, sub, DS) > kPoolLds && DS > VEC) DS /= 2;
-    if (lds_bytes(chunk, sub, DS) > 64 * 1024) return hipErrorInvalidValue;
+    PoolShape ps;
+    if (!pool_shape(g, dtype, &ps)) return hipErrorInvalidValue;
+    const int64_t chunk = ps.chunk, sub = ps.sub;
+    const int DS = ps.DS;
     P.chunk = (int)chunk; P.sub = (int)sub; P.DS = DS; P.nslices = (int)(g.d / DS);
     while ((VEC << P.nv_log2) < DS) ++P.nv_log2;
     if ((VEC << P.nv_log2) != DS) return hipErrorInvalidValue;
     for (int l = 0; l < g.L; ++l) P.epc[l] = (int)(chunk / g.pw[l]);
     // the q and k blocks give the token norms when whole rows are held by 8 lanes of d / 8 elements or
     // 16 lanes of d / 16 (8 partial sums per token of a pass in LDS)
-    size_t sh = (size_t)lds_bytes(chunk, sub, DS);
+    size_t sh = (size_t)ps.lds;
     const bool fused = P.nslices == 1 && (DS == 8 * VEC || DS == 16 * VEC) && sh + (size_t)sub * 32 <= 64 * 1024;
     P.norms = fused ? norms : nullptr;
     P.part_off = (int)(sh / 4);
@@ -697,7 +729,7 @@ hipError_t launch_pool(const LhGeom& g, int dtype, const void* q, const void* k,
 hipError_t launch_scores(const LhGeom& g, const float* norms, float* sigma, hipStream_t st) {
     if (g.L < 2) return hipSuccess;
     const ScoreP P = score_params(g);
-    if (P.chunk > 16384) return hipErrorInvalidValue;   // the chunk's levels in LDS
+    if (P.chunk > kScoreMaxChunk) return hipErrorInvalidValue;   // the chunk's levels in LDS
     int64_t ent = P.chunk;
     for (int l = 1; l < g.L; ++l) ent += P.chunk / g.pw[l];
     dim3 grid((unsigned)ceil_div(g.N, P.chunk), (unsigned)g.BH);

@@ -59,7 +59,7 @@ _SZ = ctypes.c_size_t
 _SIGS = {
     "lh_make_plan": [ctypes.POINTER(LhDesc), ctypes.POINTER(LhPlan)],
     "lh_pyramid": [ctypes.POINTER(LhDesc), _VP, _VP, _VP, _VP, _SZ, _VP],
-    "lh_score_topk": [ctypes.POINTER(LhDesc), _VP, _VP, _VP, _VP, _SZ, _VP],
+    "lh_score_topk": [ctypes.POINTER(LhDesc), _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP],
     "lh_forward": [ctypes.POINTER(LhDesc), _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP],
     "lh_backward": [ctypes.POINTER(LhDesc), _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP],
     "dense_causal_attn": [ctypes.POINTER(LhDesc), _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP],
@@ -74,7 +74,7 @@ _SIGS = {
 
 (KERNEL_POOL, KERNEL_SCORE, KERNEL_TOPK, KERNEL_MAP, KERNEL_GATHER, KERNEL_ATTN_FWD, KERNEL_SCATTER_FWD,
  KERNEL_SCATTER_BWD, KERNEL_ATTN_DKDV, KERNEL_ATTN_DQ, KERNEL_GATHER_POOL_BWD, KERNEL_TRANSPOSE,
- KERNEL_DENSE_PREP, KERNEL_QKV_FWD, KERNEL_QKV_BWD) = range(15)
+ KERNEL_DENSE_PREP, KERNEL_QKV_FWD, KERNEL_QKV_BWD, KERNEL_NORM) = range(16)
 
 
 def header_functions() -> list:
@@ -151,8 +151,9 @@ def lh_pyramid(desc, q, k, v, pyr, stream=None):
                                      _stream(stream)), "lh_pyramid")
 
 
-def lh_score_topk(desc, pyr, gidx, gpos, ws, stream=None):
-    _check(load_library().lh_score_topk(ctypes.byref(desc), _p(pyr), _p(gidx), _p(gpos), _p(ws),
+def lh_score_topk(desc, q, k, pyr, gidx, gpos, ws, stream=None):
+    """pyr may be None: the token norms are then computed from q and k."""
+    _check(load_library().lh_score_topk(ctypes.byref(desc), _p(q), _p(k), _p(pyr), _p(gidx), _p(gpos), _p(ws),
                                         _nbytes(ws), _stream(stream)), "lh_score_topk")
 
 
@@ -218,11 +219,14 @@ class LighthouseLayer:
         self.gpos = torch.empty((B, H, P.M_total), dtype=torch.int32, device=device)
         self.shape = (B, H, N, d)
 
-    def forward(self, q, k, v, o, stream=None, select=True):
+    def forward(self, q, k, v, o, stream=None, select=True, norms_from_pyramid=True):
+        """norms_from_pyramid=False scores straight from q and k (the token norms
+        are then computed again rather than taken from the pyramid buffer)."""
         if self.pyr is not None:
             lh_pyramid(self.desc, q, k, v, self.pyr, stream)
         if select:
-            lh_score_topk(self.desc, self.pyr, self.gidx, self.gpos, self.sel_ws, stream)
+            lh_score_topk(self.desc, q, k, self.pyr if norms_from_pyramid else None, self.gidx, self.gpos,
+                          self.sel_ws, stream)
         lh_forward(self.desc, q, k, v, self.pyr, self.gidx, self.gpos, o, self.fwd_ws, stream)
 
     def backward(self, dout, dq, dk, dv, stream=None):

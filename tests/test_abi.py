@@ -67,6 +67,7 @@ def test_plan_golden_s():
     ((1, 1, 64, 128, 2, 2, 1, 0), lh.LH_E_UNSUPPORTED),  # f32 with d = 128 not built
     ((1, 1, 8, 64, 4, 3, 1, 1), lh.LH_E_ARG),          # p^(L-1) > N
     ((1, 1, 1 << 25, 64, 2, 1, 1, 1), lh.LH_E_UNSUPPORTED),  # L = 1: S = 2^25 rows of 128 B reach 2^32 bytes
+    ((1, 1, 8 ** 5, 64, 8, 6, 1, 1), lh.LH_E_UNSUPPORTED),   # p^(L-1) = 32768: a score chunk exceeds the LDS
 ])
 def test_plan_rejects(args, code):
     with pytest.raises(lh.LighthouseError) as e:
@@ -85,8 +86,11 @@ def test_entry_points_validate_before_launch():
     D = ctypes.byref(desc)
     # null pointers
     assert _call("lh_pyramid", D, None, FAKE, FAKE, FAKE, plan.pyr_bytes, None) == lh.LH_E_ARG
-    assert _call("lh_score_topk", D, FAKE, None, FAKE, FAKE, plan.sel_ws_bytes, None) == lh.LH_E_ARG
-    assert _call("lh_score_topk", D, None, FAKE, FAKE, FAKE, plan.sel_ws_bytes, None) == lh.LH_E_ARG   # no pyramid
+    assert _call("lh_score_topk", D, FAKE, FAKE, FAKE, FAKE, None, FAKE, plan.sel_ws_bytes, None) == lh.LH_E_ARG
+    assert _call("lh_score_topk", D, None, FAKE, FAKE, FAKE, FAKE, FAKE, plan.sel_ws_bytes, None) == lh.LH_E_ARG  # no q
+    assert _call("lh_score_topk", D, FAKE, None, None, FAKE, FAKE, FAKE, plan.sel_ws_bytes, None) == lh.LH_E_ARG  # no k
+    assert _call("lh_score_topk", D, FAKE, FAKE, FAKE + 4, FAKE, FAKE, FAKE, plan.sel_ws_bytes,
+                 None) == lh.LH_E_ARG   # misaligned (optional) pyramid
     assert _call("lh_forward", D, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, plan.fwd_ws_bytes, None) == lh.LH_E_ARG
     assert _call("lh_backward", D, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, plan.bwd_ws_bytes, None) == lh.LH_E_ARG
     # misaligned pointers
@@ -94,7 +98,8 @@ def test_entry_points_validate_before_launch():
     assert _call("dense_causal_attn", D, FAKE, FAKE, FAKE, FAKE, FAKE + 4, FAKE, plan.dense_fwd_ws_bytes, None) == lh.LH_E_ARG
     # short workspaces
     assert _call("lh_pyramid", D, FAKE, FAKE, FAKE, FAKE, plan.pyr_bytes - 1, None) == lh.LH_E_WORKSPACE
-    assert _call("lh_score_topk", D, FAKE, FAKE, FAKE, FAKE, plan.sel_ws_bytes - 1, None) == lh.LH_E_WORKSPACE
+    assert _call("lh_score_topk", D, FAKE, FAKE, None, FAKE, FAKE, FAKE, plan.sel_ws_bytes - 1,
+                 None) == lh.LH_E_WORKSPACE
     assert _call("lh_forward", D, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, plan.fwd_ws_bytes - 1, None) == lh.LH_E_WORKSPACE
     assert _call("lh_backward", D, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, plan.bwd_ws_bytes - 1, None) == lh.LH_E_WORKSPACE
     assert _call("dense_causal_attn", D, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, plan.dense_fwd_ws_bytes - 1, None) == lh.LH_E_WORKSPACE
@@ -130,10 +135,19 @@ def test_tensor_marshalling_rejects_host_tensors():
         lh.lh_pyramid(desc, t, t, t, t)
 
 
+@pytest.mark.parametrize("N,p,L,d,dt", [(4 ** 7, 4, 8, 64, 1), (4 ** 7, 4, 8, 128, 1), (4 ** 7, 4, 8, 64, 0),
+                                         (3 ** 8, 3, 8, 64, 1), (2 ** 14, 128, 3, 64, 1), (8 ** 4, 8, 5, 128, 1)])
+def test_deep_pyramids_plan(N, p, L, d, dt):
+    """Deep pyramids up to p^(L-1) = 16384 plan (the pooling pass then takes
+    short passes over sliced rows) and match the oracle's sizes."""
+    plan = lh.lh_make_plan(lh.make_desc(1, 1, N, d, p, L, 1, dt))
+    assert plan.S == orc.make_plan(N, p, L, 1).S
+
+
 def test_probe_hook_validates_kernel_id():
     lib = lh.load_library()
     assert lib.lh_set_probe(-1, None, None) == lh.LH_OK
-    assert lib.lh_set_probe(15, None, None) == lh.LH_E_ARG
+    assert lib.lh_set_probe(lh.KERNEL_NORM + 1, None, None) == lh.LH_E_ARG
     assert lib.lh_set_probe(-2, None, None) == lh.LH_E_ARG
     assert lib.lh_set_probe(lh.KERNEL_ATTN_DKDV, None, None) == lh.LH_OK   # null events: off
 

@@ -32,6 +32,9 @@ SMALL = [
     # a partial last chunk)
     W("pyr_f32", 1, 2, 2048, 64, "f32", 4, 4, 256, 110, False),
     W("pyr_p3_d128_bf16", 1, 2, 1350, 128, "bf16", 3, 4, 200, 111, True),
+    # p^(L-1) = 16384: no pass of the pooling chunk fits whole rows, so it takes passes of
+    # p^2 tokens over rows sliced to 8 elements
+    W("p4_L8_bf16", 1, 1, 16384, 64, "bf16", 4, 8, 3, 114, True),
 ]
 
 
@@ -121,6 +124,31 @@ def test_layer_on_a_side_stream():
     got = run(torch.cuda.Stream())
     for name, a, b in zip(("o", "dq", "dk", "dv", "gidx", "gpos"), ref, got):
         assert torch.equal(a, b), f"{name} differs on a side stream"
+
+
+FROM_QK = [SMALL[0], SMALL[1], SMALL[3], SMALL[9], inputs.WORKLOADS["mid_bf16"]]
+
+
+@pytest.mark.parametrize("w", FROM_QK, ids=lambda w: w.name)
+def test_scores_from_q_and_k(w):
+    """lh_score_topk given q and k and no pyramid buffer computes the token
+    norms itself: the selection matches the oracle bit for bit and equals the
+    one scored from the norms lh_pyramid leaves."""
+    say(f"[score from q, k] {w}")
+    q, k, v, dout = _data(w)
+    dt = inputs.TORCH_DTYPE[w.dtype]
+    layer = lh.LighthouseLayer(w.B, w.H, w.N, w.d, w.p, w.L, w.k, dt)
+    qd, kd, vd = (x.cuda() for x in (q, k, v))
+    o1, o2 = torch.empty_like(qd), torch.empty_like(qd)
+    layer.forward(qd, kd, vd, o1, norms_from_pyramid=False)
+    torch.cuda.synchronize()
+    g1, p1 = layer.gidx.clone(), layer.gpos.clone()
+    layer.forward(qd, kd, vd, o2)
+    torch.cuda.synchronize()
+    assert torch.equal(g1, layer.gidx) and torch.equal(p1, layer.gpos) and torch.equal(o1, o2)
+    r = type("R", (), {})()
+    r.gidx, r.gpos = g1, p1
+    compare_selection(w, q, k, r)
 
 
 @pytest.mark.parametrize("dtype,N,d", [("f32", 256, 64), ("bf16", 1000, 64), ("bf16", 777, 128)])
