@@ -159,6 +159,24 @@ lh_status lh_pyramid(const lh_desc* desc, const void* q, const void* k, const vo
 lh_status lh_score_topk(const lh_desc* desc, const void* q, const void* k, const void* pyr,
                         int32_t* gidx, int32_t* gpos, void* ws, size_t ws_bytes, void* stream);
 
+/* lh_score_topk for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same arguments and results without the ws argument.  Its workspace is
+ * one array of LH_STATIC_SCRATCH_BYTES per GPU, loaded with the library and
+ * held until the process ends; the first call on a device looks up that
+ * device's address (hipGetSymbolAddress, with the calling thread's current
+ * device, which must be the stream's).  The call allocates nothing.
+ * Returns LH_E_WORKSPACE, before any launch, when the selection needs more than
+ * that: the level scores and top-K bitmaps, plus the token norms unless pyr is
+ * given -- e.g. B*H = 16 at N = 98304 needs 15 MB from q and k; at N = 524288,
+ * 78 MB from q and k (refused) or 11 MB with pyr.  Every byte of the array a
+ * call reads is written earlier in that same call, so nothing is cleared;
+ * calls that overlap on one GPU (other streams, other threads) share the array
+ * and race. */
+#define LH_STATIC_SCRATCH_BYTES (32u << 20)
+lh_status lh_score_topk_noalloc(const lh_desc* desc, const void* q, const void* k, const void* pyr,
+                                int32_t* gidx, int32_t* gpos, void* stream);
+
 /* Stage 3 and 4 (skill card Stage 3-4; gist.science 2C).
  * Gathers the S selected triples (level 0 rows from q/k/v, coarser ones from
  * pyr), runs causal softmax attention over them (scale, causal mask with the

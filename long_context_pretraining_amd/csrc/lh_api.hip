@@ -5,6 +5,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "lh_internal.h"
 
 namespace {
@@ -197,6 +199,58 @@ hipError_t score_topk_impl(const LhGeom& g, const lh_desc* desc, const lh_plan& 
     return e;
 }
 }  // namespace
+
+// Selection workspace of lh_score_topk_noalloc: one array per GPU, loaded with
+// the library's code object and held until the process ends.  Host code never
+// passes `scratch` itself to a kernel (on the host it is only a stand-in for
+// the symbol); it uses the device address hipGetSymbolAddress gives for the
+// current device, looked up once per device and kept.
+static __device__ __align__(256) unsigned char scratch[LH_STATIC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+hipError_t scratch_address(void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return hipSuccess;
+}
+
+// Bytes of the selection workspace a call uses: the level scores, the top-K
+// bitmaps and their prefixes, and the token norms unless they come from pyr.
+size_t sel_ws_used(const LhGeom& g, bool norms_from_pyr) {
+    const size_t sz_sigma = align_up((size_t)g.BH * g.Mu * 4), sz_w = align_up((size_t)g.BH * g.words_total * 4);
+    const size_t norms = (g.L > 1 && !norms_from_pyr) ? align_up((size_t)2 * g.BH * g.N * 4) : 0;
+    return sz_sigma + 2 * sz_w + norms;
+}
+}  // namespace
+
+lh_status lh_score_topk_noalloc(const lh_desc* desc, const void* q, const void* k, const void* pyr, int32_t* gidx,
+                                int32_t* gpos, void* stream) {
+    lh_plan P;
+    LhGeom g;
+    lh_status s = plan_impl(desc, &P, &g);
+    if (s != LH_OK) return s;
+    if (!aligned(q) || !aligned(k) || !aligned(gidx) || !aligned(gpos)) return LH_E_ARG;
+    if (pyr && !aligned(pyr)) return LH_E_ARG;
+    if (sel_ws_used(g, pyr != nullptr) > (size_t)LH_STATIC_SCRATCH_BYTES) return LH_E_WORKSPACE;
+    void* ws = nullptr;
+    if (scratch_address(&ws) != hipSuccess) return LH_E_DEVICE;
+    return dev(score_topk_impl(g, desc, P, q, k, pyr, gidx, gpos, ws, (hipStream_t)stream));
+}
 
 lh_status lh_score_topk(const lh_desc* desc, const void* q, const void* k, const void* pyr, int32_t* gidx,
                         int32_t* gpos, void* ws, size_t ws_bytes, void* stream) {

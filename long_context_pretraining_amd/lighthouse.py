@@ -60,6 +60,7 @@ _SIGS = {
     "lh_make_plan": [ctypes.POINTER(LhDesc), ctypes.POINTER(LhPlan)],
     "lh_pyramid": [ctypes.POINTER(LhDesc), _VP, _VP, _VP, _VP, _SZ, _VP],
     "lh_score_topk": [ctypes.POINTER(LhDesc), _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP],
+    "lh_score_topk_noalloc": [ctypes.POINTER(LhDesc), _VP, _VP, _VP, _VP, _VP, _VP],
     "lh_forward": [ctypes.POINTER(LhDesc), _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP],
     "lh_backward": [ctypes.POINTER(LhDesc), _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP],
     "dense_causal_attn": [ctypes.POINTER(LhDesc), _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP],
@@ -155,6 +156,15 @@ def lh_score_topk(desc, q, k, pyr, gidx, gpos, ws, stream=None):
     """pyr may be None: the token norms are then computed from q and k."""
     _check(load_library().lh_score_topk(ctypes.byref(desc), _p(q), _p(k), _p(pyr), _p(gidx), _p(gpos), _p(ws),
                                         _nbytes(ws), _stream(stream)), "lh_score_topk")
+
+
+STATIC_SCRATCH_BYTES = 32 << 20
+
+
+def lh_score_topk_noalloc(desc, q, k, pyr, gidx, gpos, stream=None):
+    """lh_score_topk with the library's own per-GPU scratch array (no ws)."""
+    _check(load_library().lh_score_topk_noalloc(ctypes.byref(desc), _p(q), _p(k), _p(pyr), _p(gidx), _p(gpos),
+                                                _stream(stream)), "lh_score_topk_noalloc")
 
 
 def lh_forward(desc, q, k, v, pyr, gidx, gpos, o, fwd_ws, stream=None):

@@ -15,7 +15,8 @@ FAKE = 0x100000          # aligned, never dereferenced: every call below fails v
 def test_exports_every_header_function():
     lib = lh.load_library()
     names = lh.header_functions()
-    assert set(names) == {"lh_make_plan", "lh_pyramid", "lh_score_topk", "lh_forward", "lh_backward",
+    assert set(names) == {"lh_make_plan", "lh_pyramid", "lh_score_topk", "lh_score_topk_noalloc",
+                          "lh_forward", "lh_backward",
                           "dense_causal_attn", "dense_causal_attn_backward", "lh_status_string", "lh_set_probe",
                           "lh_qkv_plan", "lh_qkv_forward", "lh_qkv_backward"}
     for n in names:
