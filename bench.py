@@ -39,8 +39,12 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="llama530m_98k_k1536")
-    ap.add_argument("--dense-steps", type=int, default=3)
+    ap.add_argument("--dense-steps", type=int, default=5)
+    ap.add_argument("--probe-reps", type=int, default=5, help="probed steps per kernel (median)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extreme", action="store_true", help="skip the 512K-token sub-object")
+    ap.add_argument("--extreme-steps", type=int, default=5)
+    ap.add_argument("--extreme-dense", type=int, default=1, help="time one dense step at 512K (0: skip)")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="also run one plain device copy of 1 GiB (scales rocprofv3 byte counters)")
     ap.add_argument("--pmc-summary", nargs="+", metavar="DIR",
@@ -340,6 +344,214 @@ def cpu_baseline(w, q, k, v, dout, nheads=6):
                       f"of CPU time; value = B*N / (mean time per head x {heads} heads)"}
 
 
+def median(xs):
+    xs = sorted(xs)
+    return xs[len(xs) // 2] if xs else None
+
+
+def probe_kernels(lh, ev, step, names, reps, flush=None):
+    """Median HIP-event duration of each kernel in `names` over `reps` probed
+    steps (the probe records on the library's stream); with `flush` (a device
+    buffer of >= 512 MB) the library writes it just before every probed
+    launch, so the kernel starts with its inputs out of L2 and the Infinity
+    Cache."""
+    import torch
+    ids = {n: i for i, n in enumerate(KERNEL_NAMES)}
+    if flush is not None:
+        lh.lh_set_probe_flush(flush, flush.numel())
+    out = {}
+    a, b = ev.create(), ev.create()
+    for name in names:
+        ts = []
+        for _ in range(reps):
+            lh.lh_set_probe(ids[name], a, b)
+            step()
+            torch.cuda.synchronize()
+            ts.append(ev.elapsed_ms(a, b))
+        out[name] = median(ts)
+    lh.lh_set_probe(-1, None, None)
+    lh.lh_set_probe_flush(None, 0)
+    ev.destroy(a)
+    ev.destroy(b)
+    return out
+
+
+def stage_table(w, plan, kernel_ms, kernel_ms_cold, peaks):
+    """Every kernel of the step: its algorithmic rate against its roof (warm,
+    inside running steps, and cold, after a cache flush), against the vendor
+    peak and the measured one, and, where a counter summary of the current
+    sources exists, the HBM bytes it actually moves."""
+    stages = {}
+    for name, ms in kernel_ms.items():
+        b, wk, _ = algorithmic_work(name, w, plan)
+        st = {"bound": b, "ms": round(ms, 4)}
+        cold = kernel_ms_cold.get(name)
+        if b == "mfma":
+            pk = MFMA_BF16_PEAK_TFS if w.dtype == "bf16" else MFMA_F32_PEAK_TFS
+            tf = wk / (ms * 1e-3) / 1e12
+            st.update(alg_tflops=round(tf, 1), alg_frac=round(tf / pk, 3))
+            if w.dtype == "bf16" and peaks.get("mfma_bf16_tflops"):
+                st.update(alg_frac_of_measured=round(tf / peaks["mfma_bf16_tflops"], 3))
+        else:
+            gbs = wk / (ms * 1e-3) / 1e9
+            st.update(alg_gbs=round(gbs, 1))
+            if b == "hbm":
+                st.update(alg_frac=round(gbs / HBM_PEAK_GBS, 3))
+                if peaks.get("hbm_gbs"):
+                    st.update(alg_frac_of_measured=round(gbs / peaks["hbm_gbs"], 3))
+            if cold:
+                gc = wk / (cold * 1e-3) / 1e9
+                st.update(ms_cold=round(cold, 4), alg_gbs_cold=round(gc, 1))
+                if b == "hbm":
+                    st.update(alg_frac_cold=round(gc / HBM_PEAK_GBS, 3))
+        hb = stored_traffic(name, w.name)
+        if hb is not None:
+            st.update(hbm_gbs=round(hb / (ms * 1e-3) / 1e9, 1), hbm_frac=round(hb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 3))
+        stages[name] = st
+    return stages
+
+
+def measured_peaks(dev):
+    """Achievable peaks measured on this GPU, the second denominators: the
+    library's streams over 1 GiB (16-byte accesses: copy, counting bytes read
+    + written, read only, write only; the best of the three is the measured
+    HBM peak) and its loop of independent bf16 matrix products (two waves per
+    SIMD, 32768 flops per product), each the median of five timed runs."""
+    import torch
+    from long_context_pretraining_amd import lighthouse as lh
+    out = {}
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def run(fn, n=6):
+        ts = []
+        for _ in range(n):
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return median(ts[1:])
+
+    n = 1 << 30
+    out["copy_gbs"] = round(2 * n / (run(lambda: lh.lh_peak_hbm(0, dst, src, n)) * 1e-3) / 1e9, 1)
+    out["read_gbs"] = round(n / (run(lambda: lh.lh_peak_hbm(1, dst, src, n)) * 1e-3) / 1e9, 1)
+    out["write_gbs"] = round(n / (run(lambda: lh.lh_peak_hbm(2, dst, None, n)) * 1e-3) / 1e9, 1)
+    out["hbm_gbs"] = max(out["copy_gbs"], out["read_gbs"], out["write_gbs"])
+    del src, dst
+    sink = torch.empty(256 * 512, dtype=torch.float32, device=dev)
+    iters = 20000
+    ms = run(lambda: lh.lh_peak_mfma(sink, iters))
+    out["mfma_bf16_tflops"] = round(lh.PEAK_MFMA_FLOPS_PER_ITER * iters / (ms * 1e-3) / 1e12, 1)
+    out["note"] = ("1 GiB streams of 16-byte accesses (copy counts read + written bytes; hbm_gbs = best "
+                   "of copy, read, write); mfma: back-to-back independent v_mfma_f32_32x32x16_bf16, "
+                   "two waves per SIMD")
+    del sink
+    torch.cuda.empty_cache()
+    return out
+
+
+def timed_steps(step, n):
+    """Per-step durations (ms) from events on the current stream, which is the
+    library's stream here."""
+    import torch
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for a, b in evs:
+        a.record()
+        step()
+        b.record()
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in evs]
+
+
+def extreme_512k(args, ev, peaks, dev):
+    """The 512K-token layer (B=1, H=16, N=524288, d=64, bf16, p=4, L=6,
+    k=1536): step time, forward time, every kernel warm and cold, and one dense
+    causal fwd+bwd step for the speedup.  Inputs are drawn on the device with
+    torch's generator (N(0,1) times one lognormal(0, 0.5) factor per token,
+    rounded to bf16): the same distribution as the parity tests' host recipe,
+    generated where it is used."""
+    import torch
+    from long_context_pretraining_amd import inputs
+    from long_context_pretraining_amd import lighthouse as lh
+    w = inputs.WORKLOADS["extreme_512k"]
+    g = torch.Generator(device=dev)
+    g.manual_seed(w.seed)
+    shape = (w.B, w.H, w.N, w.d)
+    m = torch.exp(0.5 * torch.randn((w.B, w.H, w.N, 1), device=dev, generator=g))
+    q, k, v = ((torch.randn(shape, device=dev, generator=g) * m).to(torch.bfloat16) for _ in range(3))
+    del m
+    dout = torch.randn(shape, device=dev, generator=g).to(torch.bfloat16)
+    layer = lh.LighthouseLayer(w.B, w.H, w.N, w.d, w.p, w.L, w.k, torch.bfloat16)
+    plan = layer.plan
+    o, dq, dk, dv = (torch.empty_like(q) for _ in range(4))
+
+    def step():
+        layer.forward(q, k, v, o)
+        layer.backward(dout, dq, dk, dv)
+
+    for _ in range(2):
+        step()
+    torch.cuda.synchronize()
+    ts = timed_steps(step, args.extreme_steps)
+    fwd = timed_steps(lambda: layer.forward(q, k, v, o), args.extreme_steps)
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    kms = probe_kernels(lh, ev, step, KERNEL_NAMES, 3)
+    kms_cold = probe_kernels(lh, ev, step, [n for n in KERNEL_NAMES if not n.startswith("attn")], 3, flush)
+    del flush
+    stages = stage_table(w, plan, kms, kms_cold, peaks)
+    ms = median(ts)
+    out = {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "p": w.p, "L": w.L, "k": w.k,
+           "S": plan.S, "S_formula": plan.S_formula, "ms_per_step_median": round(ms, 4),
+           "ms_per_step_min": round(min(ts), 4), "tokens_per_s": round(w.B * w.N / (ms * 1e-3), 1),
+           "fwd_ms_median": round(median(fwd), 4), "steps": args.extreme_steps, "stages": stages,
+           "data": "synthetic, generated on the device (torch generator, seed 5)"}
+    if args.extreme_dense:
+        ddesc = lh.make_desc(w.B, w.H, w.N, w.d, w.p, 1, 1, torch.bfloat16)
+        dplan = lh.lh_make_plan(ddesc)
+        dws = torch.empty(dplan.dense_fwd_ws_bytes, dtype=torch.uint8, device=dev)
+        dwsb = torch.empty(dplan.dense_bwd_ws_bytes, dtype=torch.uint8, device=dev)
+        lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+        dense_f = lambda: lh.dense_causal_attn(ddesc, q, k, v, o, lse, dws)
+        dense_fb = lambda: (dense_f(), lh.dense_causal_attn_backward(ddesc, q, k, v, lse, dws, dout, dq, dk, dv, dwsb))
+        dense_f()
+        torch.cuda.synchronize()
+        d_fb = median(timed_steps(dense_fb, 1))
+        d_f = median(timed_steps(dense_f, 1))
+        out.update(dense_ms_per_step=round(d_fb, 2), dense_fwd_ms=round(d_f, 2),
+                   speedup_vs_dense=round(d_fb / ms, 2), speedup_fwd_vs_dense=round(d_f / median(fwd), 2))
+        del dws, dwsb, lse
+    del layer, q, k, v, dout, o, dq, dk, dv
+    torch.cuda.empty_cache()
+    return out
+
+
+def cpu_scaling(threads_all):
+    """One head of the two small workloads through the oracle with all threads
+    and with one (threadpoolctl limits the BLAS pool)."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+    from long_context_pretraining_amd import inputs
+    from oracle import lighthouse_oracle as orc
+    out = {}
+    for name in ("tiny_f32", "mid_bf16"):
+        w = inputs.WORKLOADS[name]
+        q, k, v = inputs.make_qkv(w)
+        dout = inputs.make_dout(w)
+        f = lambda t: t[0, 0].float().numpy().astype(np.float64)
+        r = {}
+        for label, nt in (("all_threads", None), ("one_thread", 1)):
+            t0 = time.perf_counter()
+            with threadpool_limits(nt):
+                st = orc.head_forward(f(q), f(k), f(v), w.p, w.L, w.k, w.dtype)
+                orc.head_backward(st, f(dout))
+            r[label + "_s"] = round(time.perf_counter() - t0, 3)
+        r["threads_all"] = threads_all
+        out[name + " (one head, fwd+bwd)"] = r
+    return out
+
+
 def main():
     args = parse()
     if args.pmc_summary:
@@ -376,35 +588,40 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    # per-kernel durations (one probed step each) to find the dominant kernel
+    # every kernel's duration: median of a few probed steps, warm (inside running steps) and, for the
+    # bandwidth-bound ones, cold (the library writes a 1 GiB buffer just before the probed launch)
     ev = HipEvents()
-    a, b = ev.create(), ev.create()
-    kernel_ms = {}
-    for kid, name in enumerate(KERNEL_NAMES):
-        lh.lh_set_probe(kid, a, b)
-        step()
-        torch.cuda.synchronize()
-        kernel_ms[name] = ev.elapsed_ms(a, b)
-    lh.lh_set_probe(-1, None, None)
+    kernel_ms = probe_kernels(lh, ev, step, KERNEL_NAMES, args.probe_reps)
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    kernel_ms_cold = probe_kernels(lh, ev, step, [n for n in KERNEL_NAMES if not n.startswith("attn")],
+                                   args.probe_reps, flush)
+    del flush
     dominant = max(kernel_ms, key=kernel_ms.get)
     dom_id = KERNEL_NAMES.index(dominant)
 
-    # timed region: exactly K steps, the dominant kernel probed in every step
+    # timed region: exactly K steps, the dominant kernel probed in every step, and each step
+    # bracketed by events on the library's stream
     starts = [ev.create() for _ in range(args.steps)]
     stops = [ev.create() for _ in range(args.steps)]
+    step_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
         lh.lh_set_probe(dom_id, starts[i], stops[i])
+        step_ev[i][0].record()
         step()
+        step_ev[i][1].record()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     lh.lh_set_probe(-1, None, None)
     elapsed = t1 - t0
     ms_step = elapsed * 1e3 / args.steps
     dom_ms = sum(ev.elapsed_ms(s, e) for s, e in zip(starts, stops)) / args.steps
+    step_ms = [a.elapsed_time(b) for a, b in step_ev]
     tokens_per_s = w.B * w.N * args.steps / elapsed
 
+    peaks = measured_peaks(dev)
     bound, work, unit = algorithmic_work(dominant, w, plan)
     if bound == "mfma":
         peak = MFMA_BF16_PEAK_TFS if w.dtype == "bf16" else MFMA_F32_PEAK_TFS
@@ -412,29 +629,16 @@ def main():
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
                 "frac": round(achieved / peak, 4), "traffic": stored_traffic(dominant, w.name), "kernel": dominant,
                 "kernel_ms": round(dom_ms, 4), "work_per_launch": work}
+        if w.dtype == "bf16":
+            roof.update(peak_measured=peaks["mfma_bf16_tflops"],
+                        frac_of_measured=round(achieved / peaks["mfma_bf16_tflops"], 4))
     else:
         achieved = work / (dom_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": stored_traffic(dominant, w.name), "kernel": dominant,
-                "kernel_ms": round(dom_ms, 4), "work_per_launch": work}
-
-    # every kernel of the step: its algorithmic rate against its roof and, where a counter
-    # summary of the current sources exists, the HBM bytes it actually moves
-    stages = {}
-    for name, ms in kernel_ms.items():
-        b, wk, _ = algorithmic_work(name, w, plan)
-        st = {"bound": b, "ms": round(ms, 4)}
-        if b == "latency":
-            st.update(alg_gbs=round(wk / (ms * 1e-3) / 1e9, 1))
-        elif b == "mfma":
-            pk = MFMA_BF16_PEAK_TFS if w.dtype == "bf16" else MFMA_F32_PEAK_TFS
-            st.update(alg_tflops=round(wk / (ms * 1e-3) / 1e12, 1), alg_frac=round(wk / (ms * 1e-3) / 1e12 / pk, 3))
-        else:
-            st.update(alg_gbs=round(wk / (ms * 1e-3) / 1e9, 1), alg_frac=round(wk / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 3))
-        hb = stored_traffic(name, w.name)
-        if hb is not None:
-            st.update(hbm_gbs=round(hb / (ms * 1e-3) / 1e9, 1), hbm_frac=round(hb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 3))
-        stages[name] = st
+                "kernel_ms": round(dom_ms, 4), "work_per_launch": work,
+                "peak_measured": peaks["hbm_gbs"], "frac_of_measured": round(achieved / peaks["hbm_gbs"], 4)}
+    stages = stage_table(w, plan, kernel_ms, kernel_ms_cold, peaks)
 
     # dense causal attention baseline on the same GPU and inputs
     ddesc = lh.make_desc(w.B, w.H, w.N, w.d, w.p, 1, 1, dt)
@@ -482,6 +686,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
+        "ms_per_step_median": round(median(step_ms), 4),
+        "ms_per_step_min": round(min(step_ms), 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -491,17 +697,25 @@ def main():
                    "S": plan.S, "S_formula": plan.S_formula},
         "speedup_vs_dense": round(dense_ms / ms_step, 3) if dense_ms else None,
         "dense_ms_per_step": round(dense_ms, 3) if dense_ms else None,
+        "dense_steps": args.dense_steps,
         "dense_tokens_per_s": round(w.B * w.N / (dense_ms * 1e-3), 1) if dense_ms else None,
         "fwd_ms": round(fwd_ms, 4),
         "dense_fwd_ms": round(dense_fwd_ms, 3) if dense_fwd_ms else None,
         "speedup_fwd_vs_dense": round(dense_fwd_ms / fwd_ms, 3) if dense_fwd_ms else None,
         "kernel_ms": {n: round(x, 4) for n, x in kernel_ms.items()},
+        "kernel_ms_note": f"median of {args.probe_reps} probed steps per kernel (HIP events on the library's stream)",
         "roofline": roof,
+        "measured_peaks": peaks,
         "stages": stages,
         "attention_block": block,
     }
+    if headline and not args.no_extreme:
+        del layer, qd, kd, vd, dod, o, dq, dk, dv, lse
+        torch.cuda.empty_cache()
+        out["extreme_512k"] = extreme_512k(args, ev, peaks, dev)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, q, k, v, dout)
+        out["cpu_baseline"]["scaling"] = cpu_scaling(out["cpu_baseline"]["cores"])
     print(json.dumps(out), flush=True)
 
 

@@ -270,6 +270,27 @@ enum {
 };
 lh_status lh_set_probe(int kernel, void* start_event, void* stop_event);
 
+/* Measurement hook, with lh_set_probe: when `bytes` > 0, every probed launch
+ * is preceded (on the same stream, before the start event) by a kernel that
+ * reads `bytes` of the device buffer `buffer`, so that the probed
+ * kernel starts with caches holding none of its inputs (>= 512 MB clears the
+ * 256 MB Infinity Cache; the buffer is read, so no dirty lines are left for
+ * the probed kernel to write back).  bytes = 0 switches it off.  Thread-local like
+ * lh_set_probe; the buffer is owned by the caller. */
+lh_status lh_set_probe_flush(void* buffer, size_t bytes);
+
+/* Measurement microbenchmarks (achievable peaks of this GPU, the second
+ * denominators of the benchmark's roofline figures; not part of the layer).
+ * lh_peak_hbm: `bytes` (a multiple of 16) streamed with 16-byte accesses,
+ * mode 0 copying src to dst (rate = 2 * bytes / time), 1 reading src only, 2
+ * writing dst only (dst must hold 16 bytes in mode 1; src may be NULL in mode
+ * 2).  lh_peak_mfma: 256 blocks of 8 waves, each wave
+ * issuing `iters` x 4 independent v_mfma_f32_32x32x16_bf16 (32768 flops
+ * each): 256 * 8 * 4 * 32768 * iters flops; out: [256 * 512] floats (device),
+ * overwritten.  Both only enqueue on `stream`. */
+lh_status lh_peak_hbm(int mode, void* dst, const void* src, size_t bytes, void* stream);
+lh_status lh_peak_mfma(float* out, int iters, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -7,6 +7,7 @@
 
 #include <mutex>
 
+#include "lh_device.h"
 #include "lh_internal.h"
 
 namespace {
@@ -125,11 +126,92 @@ float softmax_scale(const lh_desc* d) { return d->scale > 0.f ? d->scale : 1.0f 
 // other threads never see it.
 thread_local int g_probe_kernel = -1;
 thread_local hipEvent_t g_probe_start = nullptr, g_probe_stop = nullptr;
+thread_local void* g_probe_flush = nullptr;   // optional: buffer written just before the probed kernel
+thread_local size_t g_probe_flush_bytes = 0;
+
+// Reads `n16` 16-byte words of p: clean lines that take the place of whatever
+// L2 and the Infinity Cache held, so the next kernel finds none of its inputs
+// cached and has no dirty lines to write back.  The (data-dependent, never
+// taken in practice) store keeps the reads from being dropped.
+__global__ __launch_bounds__(256) void flush_kernel(const uint4* __restrict__ p, size_t n16, uint4* sink) {
+    uint4 acc = {0u, 0u, 0u, 0u};
+    for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += (size_t)gridDim.x * 256) {
+        const uint4 v = p[i];
+        acc.x ^= v.x; acc.y ^= v.y; acc.z ^= v.z; acc.w ^= v.w;
+    }
+    if (acc.x == 0x9e3779b9u && acc.y == 0x7f4a7c15u && acc.z == 0x85ebca6bu && acc.w == 0xc2b2ae35u) sink[0] = acc;
+}
+
+// Measurement microbenchmarks (lh_peak_hbm, lh_peak_mfma): plain streams of
+// 16-byte accesses, and a loop of independent bf16 matrix products: two
+// waves per SIMD (eight per block, one block per CU) each issue four
+// independent 32x32x16 products per iteration -- one wave alone cannot issue
+// them back to back, two keep the matrix core busy.
+// Streams n16 16-byte words, 8 per thread per round (all loads issued before
+// any store), non-temporal (the data is touched once): MODE 0 copies src to
+// dst, 1 only reads src (an improbable, data-dependent store keeps the
+// loads), 2 only writes dst.
+template <int MODE>
+__global__ __launch_bounds__(256) void hbm_kernel(uint4* __restrict__ dst, const uint4* __restrict__ src,
+                                                  size_t n16) {
+    constexpr int U = 8;
+    // each block streams one contiguous range, 32 KB per round
+    const size_t per = (n16 + gridDim.x - 1) / gridDim.x;
+    const size_t b0 = (size_t)blockIdx.x * per, b1 = b0 + per < n16 ? b0 + per : n16;
+    uint4 acc = {0u, 0u, 0u, 0u};
+    for (size_t i0 = b0 + threadIdx.x; i0 < b1; i0 += U * 256) {
+        uint4 v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const size_t i = i0 + u * 256;
+            v[u] = uint4{(uint32_t)i, 0u, 0u, 0u};
+            if (MODE != 2 && i < b1) v[u] = __builtin_nontemporal_load(src + i);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const size_t i = i0 + u * 256;
+            if (MODE == 1) {
+                acc.x ^= v[u].x; acc.y ^= v[u].y; acc.z ^= v[u].z; acc.w ^= v[u].w;
+            } else if (i < b1) {
+                __builtin_nontemporal_store(v[u], dst + i);
+            }
+        }
+    }
+    if (MODE == 1 && acc.x == 0x9e3779b9u && acc.y == 0x7f4a7c15u && acc.z == 0x85ebca6bu && acc.w == 0xc2b2ae35u)
+        dst[0] = acc;
+}
+constexpr int kPeakBlocks = 256;
+__global__ __launch_bounds__(512, 1) void mfma_loop_kernel(float* out, int iters) {
+    floatx16 acc[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[j] = floatx16{};
+    bf16x8 a, b;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        a[e] = (bf16)(0.001f * (float)((threadIdx.x + e) & 63));
+        b[e] = (bf16)(0.002f * (float)e);
+    }
+    for (int i = 0; i < iters; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[j], 0, 0, 0);
+    float s = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) s += acc[j][e];
+    out[(size_t)blockIdx.x * 512 + threadIdx.x] = s;   // out holds kPeakBlocks * 512 floats
+}
 
 template <class F>
 hipError_t probed(int id, hipStream_t st, F&& launch) {
     const bool on = id == g_probe_kernel && g_probe_start && g_probe_stop;
     if (on) {
+        if (g_probe_flush && g_probe_flush_bytes >= 16) {
+            flush_kernel<<<2048, 256, 0, st>>>((const uint4*)g_probe_flush, g_probe_flush_bytes / 16,
+                                               (uint4*)g_probe_flush);
+            const hipError_t f = hipGetLastError();
+            if (f != hipSuccess) return f;
+        }
         const hipError_t r = hipEventRecord(g_probe_start, st);
         if (r != hipSuccess) return r;
     }
@@ -481,6 +563,30 @@ lh_status lh_set_probe(int kernel, void* start_event, void* stop_event) {
     g_probe_kernel = (start_event && stop_event) ? kernel : -1;
     g_probe_start = (hipEvent_t)start_event;
     g_probe_stop = (hipEvent_t)stop_event;
+    return LH_OK;
+}
+
+lh_status lh_peak_hbm(int mode, void* dst, const void* src, size_t bytes, void* stream) {
+    if (mode < 0 || mode > 2 || !aligned(dst) || (mode != 2 && !aligned(src)) || bytes % 16 || !bytes)
+        return LH_E_ARG;
+    hipStream_t st = (hipStream_t)stream;
+    const size_t n16 = bytes / 16;
+    if (mode == 0) hbm_kernel<0><<<4096, 256, 0, st>>>((uint4*)dst, (const uint4*)src, n16);
+    if (mode == 1) hbm_kernel<1><<<4096, 256, 0, st>>>((uint4*)dst, (const uint4*)src, n16);
+    if (mode == 2) hbm_kernel<2><<<4096, 256, 0, st>>>((uint4*)dst, (const uint4*)src, n16);
+    return dev(hipGetLastError());
+}
+
+lh_status lh_peak_mfma(float* out, int iters, void* stream) {
+    if (!aligned(out) || iters < 1) return LH_E_ARG;
+    mfma_loop_kernel<<<kPeakBlocks, 512, 0, (hipStream_t)stream>>>(out, iters);
+    return dev(hipGetLastError());
+}
+
+lh_status lh_set_probe_flush(void* buffer, size_t bytes) {
+    if (bytes && !aligned(buffer)) return LH_E_ARG;
+    g_probe_flush = bytes ? buffer : nullptr;
+    g_probe_flush_bytes = bytes;
     return LH_OK;
 }
 

@@ -71,6 +71,9 @@ _SIGS = {
     "lh_qkv_backward": [ctypes.POINTER(LhProjDesc), _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP],
     "lh_status_string": [ctypes.c_int],
     "lh_set_probe": [ctypes.c_int, _VP, _VP],
+    "lh_set_probe_flush": [_VP, _SZ],
+    "lh_peak_hbm": [ctypes.c_int, _VP, _VP, _SZ, _VP],
+    "lh_peak_mfma": [_VP, ctypes.c_int, _VP],
 }
 
 (KERNEL_POOL, KERNEL_SCORE, KERNEL_TOPK, KERNEL_MAP, KERNEL_GATHER, KERNEL_ATTN_FWD, KERNEL_SCATTER_FWD,
@@ -105,6 +108,24 @@ def lh_set_probe(kernel: int, start_event, stop_event):
     """Record raw hipEvent_t handles around every later launch of `kernel`
     (-1 switches the hook off)."""
     _check(load_library().lh_set_probe(kernel, start_event, stop_event), "lh_set_probe")
+
+
+def lh_set_probe_flush(buffer, nbytes: int):
+    """Before every later probed launch, read nbytes of the device tensor
+    `buffer`, evicting the caches (0 switches it off)."""
+    _check(load_library().lh_set_probe_flush(_p(buffer) if nbytes else None, nbytes), "lh_set_probe_flush")
+
+
+PEAK_MFMA_FLOPS_PER_ITER = 256 * 8 * 4 * 32768
+
+
+def lh_peak_hbm(mode: int, dst, src, nbytes: int, stream=None):
+    """mode 0: copy src to dst; 1: read src; 2: write dst."""
+    _check(load_library().lh_peak_hbm(mode, _p(dst), _p(src), nbytes, _stream(stream)), "lh_peak_hbm")
+
+
+def lh_peak_mfma(out, iters: int, stream=None):
+    _check(load_library().lh_peak_mfma(_p(out), iters, _stream(stream)), "lh_peak_mfma")
 
 
 def status_string(status: int) -> str:

@@ -18,6 +18,7 @@ def test_exports_every_header_function():
     assert set(names) == {"lh_make_plan", "lh_pyramid", "lh_score_topk", "lh_score_topk_noalloc",
                           "lh_forward", "lh_backward",
                           "dense_causal_attn", "dense_causal_attn_backward", "lh_status_string", "lh_set_probe",
+                          "lh_set_probe_flush", "lh_peak_hbm", "lh_peak_mfma",
                           "lh_qkv_plan", "lh_qkv_forward", "lh_qkv_backward"}
     for n in names:
         assert hasattr(lib, n), n
@@ -151,6 +152,14 @@ def test_probe_hook_validates_kernel_id():
     assert lib.lh_set_probe(lh.KERNEL_NORM + 1, None, None) == lh.LH_E_ARG
     assert lib.lh_set_probe(-2, None, None) == lh.LH_E_ARG
     assert lib.lh_set_probe(lh.KERNEL_ATTN_DKDV, None, None) == lh.LH_OK   # null events: off
+    assert lib.lh_set_probe_flush(None, 0) == lh.LH_OK
+    assert lib.lh_set_probe_flush(FAKE + 4, 1 << 20) == lh.LH_E_ARG     # misaligned
+    assert lib.lh_set_probe_flush(None, 1 << 20) == lh.LH_E_ARG         # no buffer
+    assert lib.lh_peak_hbm(0, FAKE, FAKE, 17, None) == lh.LH_E_ARG          # not a multiple of 16
+    assert lib.lh_peak_hbm(3, FAKE, FAKE, 16, None) == lh.LH_E_ARG          # unknown mode
+    assert lib.lh_peak_hbm(0, FAKE, None, 16, None) == lh.LH_E_ARG          # copy without a source
+    assert lib.lh_peak_mfma(None, 10, None) == lh.LH_E_ARG
+    assert lib.lh_peak_mfma(FAKE, 0, None) == lh.LH_E_ARG
 
 
 def test_projection_plan_and_argument_checks():
