@@ -413,14 +413,14 @@ def stage_table(w, plan, kernel_ms, kernel_ms_cold, peaks):
 
 def measured_peaks(dev):
     """Achievable peaks measured on this GPU, the second denominators: the
-    library's streams over 1 GiB (16-byte accesses: copy, counting bytes read
+    library's streams over 2 GiB (16-byte accesses: copy, counting bytes read
     + written, read only, write only; the best of the three is the measured
     HBM peak) and its loop of independent bf16 matrix products (two waves per
     SIMD, 32768 flops per product), each the median of five timed runs."""
     import torch
     from long_context_pretraining_amd import lighthouse as lh
     out = {}
-    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    src = torch.empty(2 << 30, dtype=torch.uint8, device=dev)
     dst = torch.empty_like(src)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
 
@@ -434,7 +434,7 @@ def measured_peaks(dev):
             ts.append(e0.elapsed_time(e1))
         return median(ts[1:])
 
-    n = 1 << 30
+    n = 2 << 30
     out["copy_gbs"] = round(2 * n / (run(lambda: lh.lh_peak_hbm(0, dst, src, n)) * 1e-3) / 1e9, 1)
     out["read_gbs"] = round(n / (run(lambda: lh.lh_peak_hbm(1, dst, src, n)) * 1e-3) / 1e9, 1)
     out["write_gbs"] = round(n / (run(lambda: lh.lh_peak_hbm(2, dst, None, n)) * 1e-3) / 1e9, 1)
@@ -444,7 +444,7 @@ def measured_peaks(dev):
     iters = 20000
     ms = run(lambda: lh.lh_peak_mfma(sink, iters))
     out["mfma_bf16_tflops"] = round(lh.PEAK_MFMA_FLOPS_PER_ITER * iters / (ms * 1e-3) / 1e12, 1)
-    out["note"] = ("1 GiB streams of 16-byte accesses (copy counts read + written bytes; hbm_gbs = best "
+    out["note"] = ("2 GiB streams of 16-byte accesses (copy counts read + written bytes; hbm_gbs = best "
                    "of copy, read, write); mfma: back-to-back independent v_mfma_f32_32x32x16_bf16, "
                    "two waves per SIMD")
     del sink

@@ -148,33 +148,30 @@ __global__ __launch_bounds__(256) void flush_kernel(const uint4* __restrict__ p,
 // independent 32x32x16 products per iteration -- one wave alone cannot issue
 // them back to back, two keep the matrix core busy.
 // Streams n16 16-byte words, 8 per thread per round (all loads issued before
-// any store), non-temporal (the data is touched once): MODE 0 copies src to
-// dst, 1 only reads src (an improbable, data-dependent store keeps the
-// loads), 2 only writes dst.
+// any store) over a grid-stride of 16384 blocks: MODE 0 copies src to dst, 1
+// only reads src (an improbable, data-dependent store keeps the loads), 2 only
+// writes dst.  Loads are non-temporal and stores plain: on this GPU that pair
+// streamed fastest for buffers beyond the Infinity Cache.
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 template <int MODE>
-__global__ __launch_bounds__(256) void hbm_kernel(uint4* __restrict__ dst, const uint4* __restrict__ src,
+__global__ __launch_bounds__(256) void hbm_kernel(u32x4_t* __restrict__ dst, const u32x4_t* __restrict__ src,
                                                   size_t n16) {
     constexpr int U = 8;
-    // each block streams one contiguous range, 32 KB per round
-    const size_t per = (n16 + gridDim.x - 1) / gridDim.x;
-    const size_t b0 = (size_t)blockIdx.x * per, b1 = b0 + per < n16 ? b0 + per : n16;
-    uint4 acc = {0u, 0u, 0u, 0u};
-    for (size_t i0 = b0 + threadIdx.x; i0 < b1; i0 += U * 256) {
-        uint4 v[U];
+    const size_t stride = (size_t)gridDim.x * 256;
+    u32x4_t acc = {0u, 0u, 0u, 0u};
+    for (size_t i0 = (size_t)blockIdx.x * 256 + threadIdx.x; i0 < n16; i0 += U * stride) {
+        u32x4_t v[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const size_t i = i0 + u * 256;
-            v[u] = uint4{(uint32_t)i, 0u, 0u, 0u};
-            if (MODE != 2 && i < b1) v[u] = __builtin_nontemporal_load(src + i);
+            const size_t i = i0 + u * stride;
+            v[u] = u32x4_t{(uint32_t)i, 1u, 2u, 3u};
+            if (MODE != 2 && i < n16) v[u] = __builtin_nontemporal_load(src + i);
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const size_t i = i0 + u * 256;
-            if (MODE == 1) {
-                acc.x ^= v[u].x; acc.y ^= v[u].y; acc.z ^= v[u].z; acc.w ^= v[u].w;
-            } else if (i < b1) {
-                __builtin_nontemporal_store(v[u], dst + i);
-            }
+            const size_t i = i0 + u * stride;
+            if (MODE == 1) acc ^= v[u];
+            else if (i < n16) dst[i] = v[u];
         }
     }
     if (MODE == 1 && acc.x == 0x9e3779b9u && acc.y == 0x7f4a7c15u && acc.z == 0x85ebca6bu && acc.w == 0xc2b2ae35u)
@@ -571,9 +568,11 @@ lh_status lh_peak_hbm(int mode, void* dst, const void* src, size_t bytes, void* 
         return LH_E_ARG;
     hipStream_t st = (hipStream_t)stream;
     const size_t n16 = bytes / 16;
-    if (mode == 0) hbm_kernel<0><<<4096, 256, 0, st>>>((uint4*)dst, (const uint4*)src, n16);
-    if (mode == 1) hbm_kernel<1><<<4096, 256, 0, st>>>((uint4*)dst, (const uint4*)src, n16);
-    if (mode == 2) hbm_kernel<2><<<4096, 256, 0, st>>>((uint4*)dst, (const uint4*)src, n16);
+    u32x4_t* d = (u32x4_t*)dst;
+    const u32x4_t* s = (const u32x4_t*)src;
+    if (mode == 0) hbm_kernel<0><<<16384, 256, 0, st>>>(d, s, n16);
+    if (mode == 1) hbm_kernel<1><<<16384, 256, 0, st>>>(d, s, n16);
+    if (mode == 2) hbm_kernel<2><<<16384, 256, 0, st>>>(d, s, n16);
     return dev(hipGetLastError());
 }
 
