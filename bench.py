@@ -70,7 +70,7 @@ KERNEL_SYMBOLS = {
     "topk": (("topk_kernel",), "select"), "map": (("map_kernel",), "select"),
     "gather": (("gather_kernel",), "scatter"), "attn_fwd": (("attn_fwd_kernel",), "attn"),
     "scatter_fwd": (("scatter_fwd_kernel",), "scatter"),
-    "scatter_bwd": ((("scatter_bwd_kernel",), ("scatter_bwd_pyr_kernel", "slot_dot_kernel")), "scatter"),
+    "scatter_bwd": ((("scatter_bwd_kernel",), ("scatter_bwd_tree_kernel", "slot_dot_kernel")), "scatter"),
     "attn_dkdv": (("attn_dkdv_kernel",), "attn"), "attn_dq": (("attn_dq_kernel",), "attn"),
     "gather_pool_bwd": (("gpool_bwd_kernel",), "scatter"),
 }

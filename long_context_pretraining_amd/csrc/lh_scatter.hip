@@ -444,34 +444,41 @@ __global__ __launch_bounds__(kThreads) void gpool_bwd_kernel(const float* __rest
 // past S), and the backward prologue (transposed dO and D = rowsum(dO * O)).
 // ---------------------------------------------------------------------------
 // ---------------------------------------------------------------------------
-// Scatter backward as a pyramid (the form used when whole rows fit the LDS).
-// With t' = t + 1, the range R(l, i) = [(i+1) p^l - 1, (i+2) p^l - 2] is the
-// aligned block i+1 of level l of the shifted sequence dout'[t'] = dout[t'-1]
-// (dout'[0] = 0, and tokens past N - 1 are 0, which is the clipping), so every
-// range sum is an entry of the plain sum pyramid of dout': children summed in
-// index order in f32, level by level.  A block builds that pyramid for one
-// aligned chunk of t' in LDS -- level 1 in passes of P.sub tokens, like the
-// pooling pass -- and stores every entry whose slot is selected as dOg (one
-// rounding to T).  dout is read once instead of once per covering level.
+// Scatter backward as a pyramid (the form used when the chunk's coarse levels
+// fit the LDS).  With t' = t + 1, the range R(l, i) = [(i+1) p^l - 1,
+// (i+2) p^l - 2] is the aligned block i+1 of level l of the shifted sequence
+// dout'[t'] = dout[t'-1] (dout'[0] = 0, and tokens past N - 1 are 0, which is
+// the clipping), so every range sum is an entry of the plain sum pyramid of
+// dout': children summed in index order in f32, level by level.  dout is read
+// once.  A block owns one aligned chunk of t' (a multiple of p^(L-1) and of
+// p^2); each group of VEC-element lanes owns p^2 consecutive rows of it: it
+// issues all p^2 row loads at once and forms levels 0, 1 and 2 in registers.
+// Levels 3 .. L-1 are summed from the level-2 rows kept in LDS.  Every entry
+// whose slot is selected is stored as dOg (one rounding to T); level-0 slots
+// and level-1 slots of the chunk are staged in LDS, loaded before the rows.
 // D and -LSE/scale follow in slot order (slot_dot_kernel).
 // ---------------------------------------------------------------------------
-struct ShiftP {
-    int chunk;   // t' positions per block: a multiple of p^(L-1)
-    int sub;     // t' positions per level-1 pass: chunk, or p^j (j >= 2) dividing it
+struct TreeP {
+    int chunk;     // t' positions per block
+    int s1_off;    // LDS: level-0 slots at 0 (chunk ints), level-1 slots at s1_off (chunk / p ints)
+    int rows_off;  // LDS byte offset of the f32 rows of levels 2 .. L-2
 };
 
-template <typename T>
-__global__ __launch_bounds__(kThreads) void scatter_bwd_pyr_kernel(const T* __restrict__ dout,
-                                                                   const int32_t* __restrict__ gpos,
-                                                                   T* __restrict__ dog, MapGeo G, ShiftP P) {
-    extern __shared__ __align__(16) float lds[];
-    constexpr int VEC = V16<T>::N;
+template <typename T, int D, int P>
+__global__ __launch_bounds__(1024) void scatter_bwd_tree_kernel(const T* __restrict__ dout,
+                                                                const int32_t* __restrict__ gpos,
+                                                                T* __restrict__ dog, MapGeo G, TreeP TP) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    constexpr int VEC = V16<T>::N, NVEC = D / VEC, U = P * P;
     typedef typename V16<T>::type VT;
-    const int d = (int)G.d, nvec = d / VEC, p = G.p;
+    int32_t* s0l = reinterpret_cast<int32_t*>(smem);
+    int32_t* s1l = s0l + TP.s1_off;
+    float* lrow = reinterpret_cast<float*>(smem + TP.rows_off);
+    const int C = TP.chunk, nthr = blockDim.x, tid = threadIdx.x;
     const int64_t bh = blockIdx.y;
-    const int64_t c0 = (int64_t)blockIdx.x * P.chunk;   // first t' of the chunk
-    const T* dh = dout + bh * G.N * G.d;
-    T* dgh = dog + bh * G.S * G.d;
+    const int64_t c0 = (int64_t)blockIdx.x * C;   // first t' of the chunk
+    const T* dh = dout + bh * G.N * D;
+    T* dgh = dog + bh * G.S * D;
     const int32_t* gp = gpos + bh * G.M_total;
 
     // entry (l, k) of the shifted pyramid is range entry i = k - 1
@@ -483,122 +490,104 @@ __global__ __launch_bounds__(kThreads) void scatter_bwd_pyr_kernel(const T* __re
         VT r;
 #pragma unroll
         for (int e = 0; e < VEC; ++e) r[e] = static_cast<T>(acc[e]);
-        *reinterpret_cast<VT*>(dgh + (int64_t)slot * G.d + vv * VEC) = r;
-    };
-    auto load_row = [&](int64_t tp, int vv, float* x) {   // dout'[tp], 0 outside [1, N]
-        VT v = {};
-        if (tp >= 1 && tp <= G.N) v = *reinterpret_cast<const VT*>(dh + (tp - 1) * G.d + vv * VEC);
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) x[e] = to_f(v[e]);
+        *reinterpret_cast<VT*>(dgh + (int64_t)slot * D + vv * VEC) = r;
     };
 
-    if (G.L < 2) {   // level 0 only: every selected token copied
-        for (int task = threadIdx.x; task < P.chunk * nvec; task += kThreads) {
-            const int e = task / nvec, vv = task % nvec;
-            const int32_t slot = slot_of(0, c0 + e);
-            float x[VEC];
-            load_row(c0 + e, vv, x);
-            if (slot >= 0) store(slot, vv, x);
-        }
-        return;
+    // Slots of the chunk's level-0 and level-1 entries, requested first, then
+    // the rows.  All these loads are unconditional (clamped indices, results
+    // masked afterwards), so the wait for the slots leaves the rows in flight.
+    const int n1 = C / P;
+    const int64_t M0 = G.off[1] - G.off[0], M1 = G.L > 1 ? G.off[2] - G.off[1] : 0;
+    int32_t sv[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int i = tid + j * nthr;
+        const bool lv0 = i < C;
+        const int64_t e = lv0 ? c0 + i - 1 : c0 / P + (i - C) - 1;   // range entry i = k - 1
+        const int64_t m = lv0 ? M0 : M1;
+        const bool ok = i < C + n1 && e >= 0 && e < m;
+        const int64_t idx = (lv0 ? G.off[0] : G.off[1]) + (ok ? e : 0);
+        const int32_t v = gp[idx];
+        sv[j] = ok ? v : -1;
     }
-    const int n1s = P.sub / p, n2 = P.chunk / (p * p);
-    float* l2 = lds + n1s * d;
-    for (int sc = 0; sc < P.chunk; sc += P.sub) {
-        // level 1 of the pass (and the level-0 tokens it reads): two entries per
-        // step, their children in batches of 4, every row load and slot lookup
-        // issued before any is used
-        const int64_t k1 = (c0 + sc) / p;
-        const int nt = n1s * nvec;
-        for (int ta = threadIdx.x; ta < nt; ta += 2 * kThreads) {
-            const int task[2] = {ta, ta + kThreads < nt ? ta + kThreads : ta};
-            const bool live1 = ta + kThreads < nt;
-            int e[2], vv[2];
-            int32_t s1[2];
-            float acc[2][VEC];
+    const int units = C / U, per = nthr / NVEC;
+    const int vv = tid % NVEC;
+    int u = tid / NVEC;
+    VT x[U];
+    auto load_unit = [&](int uu) {
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                e[j] = task[j] / nvec;
-                vv[j] = task[j] % nvec;
-                s1[j] = slot_of(1, k1 + e[j]);
-#pragma unroll
-                for (int i = 0; i < VEC; ++i) acc[j][i] = 0.f;
-            }
-            for (int cb = 0; cb < p; cb += 4) {
-                float x[2][4][VEC];
-                int32_t s0[2][4];
-#pragma unroll
-                for (int u = 0; u < 4; ++u)
-#pragma unroll
-                    for (int j = 0; j < 2; ++j) {
-                        const int64_t tp = (k1 + e[j]) * p + cb + u;
-                        s0[j][u] = -1;
-                        if (cb + u < p) {
-                            load_row(tp, vv[j], x[j][u]);
-                            s0[j][u] = slot_of(0, tp);
-                        }
-                    }
-#pragma unroll
-                for (int u = 0; u < 4; ++u)
-#pragma unroll
-                    for (int j = 0; j < 2; ++j)
-                        if (cb + u < p) {
-#pragma unroll
-                            for (int i = 0; i < VEC; ++i) acc[j][i] += x[j][u][i];
-                            if (s0[j][u] >= 0 && (j == 0 || live1)) store(s0[j][u], vv[j], x[j][u]);
-                        }
-            }
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                if (j == 1 && !live1) continue;
-                if (G.L > 2)
-#pragma unroll
-                    for (int i = 0; i < VEC; ++i) lds[e[j] * d + vv[j] * VEC + i] = acc[j][i];
-                if (s1[j] >= 0) store(s1[j], vv[j], acc[j]);
-            }
+        for (int j = 0; j < U; ++j) {
+            const int64_t tp = c0 + (int64_t)uu * U + j;
+            const bool ok = uu < units && tp >= 1 && tp <= G.N;
+            const int64_t row = ok ? tp - 1 : 0;
+            const VT v = __builtin_nontemporal_load(reinterpret_cast<const VT*>(dh + row * D + vv * VEC));
+            x[j] = ok ? v : VT{};
         }
-        if (G.L <= 2) continue;
-        __syncthreads();
-        const int64_t k2 = (c0 + sc) / (p * p);
-        const int e2 = sc / (p * p);
-        for (int task = threadIdx.x; task < (n1s / p) * nvec; task += kThreads) {
-            const int e = task / nvec, vv = task % nvec;
-            const int32_t s2 = slot_of(2, k2 + e);
-            float acc[VEC];
+    };
+    load_unit(u);
 #pragma unroll
-            for (int i = 0; i < VEC; ++i) acc[i] = 0.f;
-            for (int c = 0; c < p; ++c)
+    for (int j = 0; j < 4; ++j) {
+        const int i = tid + j * nthr;
+        if (i < C) s0l[i] = sv[j];
+        else if (i < C + n1) s1l[i - C] = sv[j];
+    }
+    __syncthreads();
+    for (; u < units; u += per) {
+        if (u != tid / NVEC) load_unit(u);
+        float a2[VEC];
 #pragma unroll
-                for (int i = 0; i < VEC; ++i) acc[i] += lds[(e * p + c) * d + vv * VEC + i];
+        for (int e = 0; e < VEC; ++e) a2[e] = 0.f;
+#pragma unroll
+        for (int i = 0; i < P; ++i) {
+            float a1[VEC];
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) a1[e] = 0.f;
+#pragma unroll
+            for (int c = 0; c < P; ++c) {
+                const int j = i * P + c;
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) a1[e] += to_f(x[j][e]);
+                const int32_t s0 = s0l[u * U + j];
+                if (s0 >= 0) *reinterpret_cast<VT*>(dgh + (int64_t)s0 * D + vv * VEC) = x[j];
+            }
+            if (G.L > 1) {
+                const int32_t s1 = s1l[u * P + i];
+                if (s1 >= 0) store(s1, vv, a1);
+            }
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) a2[e] += a1[e];
+        }
+        if (G.L > 2) {
+            const int32_t s2 = slot_of(2, c0 / U + u);
+            if (s2 >= 0) store(s2, vv, a2);
             if (G.L > 3)
 #pragma unroll
-                for (int i = 0; i < VEC; ++i) l2[(e2 + e) * d + vv * VEC + i] = acc[i];
-            if (s2 >= 0) store(s2, vv, acc);
+                for (int e = 0; e < VEC; ++e) lrow[u * D + vv * VEC + e] = a2[e];
         }
-        __syncthreads();   // the level-1 scratch is reused by the next pass
     }
     // levels 3 .. L-1 from the level below, kept in LDS
-    int prev_off = n1s * d, cur_off = prev_off + n2 * d, n_prev = n2;
+    int prev = 0, cur = units * D, n_prev = units;
     for (int l = 3; l < G.L; ++l) {
-        const int n = n_prev / p;
+        __syncthreads();
+        const int n = n_prev / P;
         const int64_t kl = c0 / G.pw[l];
-        for (int task = threadIdx.x; task < n * nvec; task += kThreads) {
-            const int e = task / nvec, vv = task % nvec;
-            const int32_t sl = slot_of(l, kl + e);
+        for (int task = tid; task < n * NVEC; task += nthr) {
+            const int e = task / NVEC, w = task % NVEC;
             float acc[VEC];
 #pragma unroll
             for (int i = 0; i < VEC; ++i) acc[i] = 0.f;
-            for (int c = 0; c < p; ++c)
 #pragma unroll
-                for (int i = 0; i < VEC; ++i) acc[i] += lds[prev_off + (e * p + c) * d + vv * VEC + i];
+            for (int c = 0; c < P; ++c)
+#pragma unroll
+                for (int i = 0; i < VEC; ++i) acc[i] += lrow[prev + (e * P + c) * D + w * VEC + i];
             if (l + 1 < G.L)
 #pragma unroll
-                for (int i = 0; i < VEC; ++i) lds[cur_off + e * d + vv * VEC + i] = acc[i];
-            if (sl >= 0) store(sl, vv, acc);
+                for (int i = 0; i < VEC; ++i) lrow[cur + e * D + w * VEC + i] = acc[i];
+            const int32_t sl = slot_of(l, kl + e);
+            if (sl >= 0) store(sl, w, acc);
         }
-        __syncthreads();
-        prev_off = cur_off;
-        cur_off += n * d;
+        prev = cur;
+        cur += n * D;
         n_prev = n;
     }
 }
@@ -620,8 +609,13 @@ __global__ __launch_bounds__(kThreads) void slot_dot_kernel(const T* __restrict_
         float dp = 0.f;
         if (s0 + sl < S) {
             const int64_t row = (bh * S + s0 + sl) * d + vv * VEC;
-            const VT v = *reinterpret_cast<const VT*>(dog + row);
-            const float* ov = og + row;
+            const VT v = __builtin_nontemporal_load(reinterpret_cast<const VT*>(dog + row));
+            float ov[VEC];
+#pragma unroll
+            for (int e = 0; e < VEC; e += 4) {
+                const floatx4 o4 = __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(og + row + e));
+                ov[e] = o4[0]; ov[e + 1] = o4[1]; ov[e + 2] = o4[2]; ov[e + 3] = o4[3];
+            }
 #pragma unroll
             for (int e = 0; e < VEC; ++e) dp += to_f(v[e]) * ov[e];
         }
@@ -748,23 +742,51 @@ hipError_t launch_scatter_fwd(const LhGeom& g, int dtype, const float* og, const
 }
 
 namespace {
-// Chunk and level-1 pass of the pyramid form of the scatter backward: whole
-// rows of f32 in at most 48 KB of LDS (one pass's level 1 plus the chunk's
-// levels 2 .. L-1).  chunk = 0 when no choice fits.
-ShiftP shift_plan(const LhGeom& g) {
-    auto bytes = [&](int64_t ch, int64_t sub) {
-        int64_t ent = g.L > 2 ? sub / g.p : 0;
-        for (int l = 2; l < g.L - 1; ++l) ent += ch / g.pw[l];   // the coarsest level is not kept
-        return ent * g.d * 4;
+constexpr int kTreeLds = 48 * 1024;
+
+// Block shape of the pyramid form: one pass of 256 threads where the chunk
+// allows (each NVEC-lane group on p^2 rows), the chunk rounded up to a
+// multiple of p^(L-1); chunk = 0 when p, d or the LDS rule it out.
+struct TreeLaunch {
+    TreeP P;
+    int threads;
+    size_t lds;
+};
+TreeLaunch tree_plan(const LhGeom& g, int dtype) {
+    TreeLaunch t{};
+    if (g.L < 2 || g.p < 2 || g.p > 4 || (g.d != 64 && g.d != 128)) return t;
+    const int64_t nvec = g.d / (dtype == LH_BF16 ? 8 : 4), U = (int64_t)g.p * g.p;
+    const int64_t m = g.pw[g.L - 1] > U ? g.pw[g.L - 1] : U;
+    int64_t C = (256 / nvec) * U;
+    C = (C + m - 1) / m * m;
+    int64_t threads = C / U * nvec;
+    threads = threads > 1024 ? 1024 : (threads + 63) / 64 * 64;
+    const int64_t n1 = C / g.p;
+    if (C + n1 > 4 * threads || C > (1 << 20)) return t;   // the kernel stages the slots in four loads per thread
+    const int64_t s1_off = C, rows_off = ((C + n1) * 4 + 15) & ~(int64_t)15;
+    int64_t rows = 0;
+    for (int l = 2; l + 1 < g.L; ++l) rows += C / g.pw[l];
+    const int64_t lds = rows_off + rows * g.d * 4;
+    if (lds > kTreeLds) return t;
+    t.P = TreeP{(int)C, (int)s1_off, (int)rows_off};
+    t.threads = (int)threads;
+    t.lds = (size_t)lds;
+    return t;
+}
+
+template <typename T>
+hipError_t launch_tree(const LhGeom& g, const TreeLaunch& t, const void* dout, const int32_t* gpos, void* dog,
+                       const MapGeo& G, hipStream_t st) {
+    dim3 grid((unsigned)(g.N / t.P.chunk + 1), (unsigned)g.BH);
+    auto go = [&](auto kern) {
+        kern<<<grid, t.threads, t.lds, st>>>((const T*)dout, gpos, (T*)dog, G, t.P);
+        return hipGetLastError();
     };
-    constexpr int64_t kMax = 48 * 1024;
-    int64_t chunk = g.pw[g.L - 1];
-    while (chunk < 256) chunk *= 2;
-    while (bytes(chunk, chunk) > kMax && chunk > g.pw[g.L - 1]) chunk /= 2;
-    int64_t sub = chunk;
-    for (int j = g.L - 2; j >= 2 && bytes(chunk, sub) > kMax; --j) sub = g.pw[j];
-    if (bytes(chunk, sub) > kMax || chunk > (1 << 20)) return ShiftP{0, 0};
-    return ShiftP{(int)chunk, (int)sub};
+    if (g.d == 64)
+        return g.p == 2 ? go(scatter_bwd_tree_kernel<T, 64, 2>)
+             : g.p == 3 ? go(scatter_bwd_tree_kernel<T, 64, 3>) : go(scatter_bwd_tree_kernel<T, 64, 4>);
+    return g.p == 2 ? go(scatter_bwd_tree_kernel<T, 128, 2>)
+         : g.p == 3 ? go(scatter_bwd_tree_kernel<T, 128, 3>) : go(scatter_bwd_tree_kernel<T, 128, 4>);
 }
 }  // namespace
 
@@ -772,31 +794,19 @@ hipError_t launch_scatter_bwd(const LhGeom& g, int dtype, const void* dout, cons
                               const int32_t* gpos, const float* lse, float scale, void* dog, void* dogT, float* nd,
                               float* nl, hipStream_t st) {
     const MapGeo G = make_geo(g);
-    const ShiftP SP = shift_plan(g);
-    // The slot-centric form reads each selected entry's range: sum over levels of
-    // (selected entries) x p^l rows, i.e. p k_(l+1) entries at l < L-1 and all M_(L-1)
-    // at the top.  The pyramid form reads dO once but in short, latency-bound blocks;
-    // measured, it wins once the slot form re-reads dO about 2.75 times or more
-    // (512K tokens, L = 6: 3.0x, 0.72 -> 0.36 ms) and ties at 2.3x (98K, L = 4).
-    int64_t rows = g.M[g.L - 1] * g.pw[g.L - 1];
-    for (int l = 0; l + 1 < g.L; ++l) rows += g.p * g.k_eff[l + 1] * g.pw[l];
-    if (SP.chunk > 0 && 4 * rows >= 11 * g.N) {
+    const TreeLaunch TL = tree_plan(g, dtype);
+    if (TL.P.chunk > 0) {
         // pyramid form: every t' in [0, N] lies in one of the chunks
-        dim3 grid((unsigned)(g.N / SP.chunk + 1), (unsigned)g.BH);
-        int64_t ent = g.L > 2 ? SP.sub / g.p : 0;
-        for (int l = 2; l < g.L - 1; ++l) ent += SP.chunk / g.pw[l];
-        const size_t sh = (size_t)ent * g.d * 4;
-        if (dtype == LH_BF16)
-            scatter_bwd_pyr_kernel<bf16><<<grid, kThreads, sh, st>>>((const bf16*)dout, gpos, (bf16*)dog, G, SP);
-        else
-            scatter_bwd_pyr_kernel<float><<<grid, kThreads, sh, st>>>((const float*)dout, gpos, (float*)dog, G, SP);
+        hipError_t e = dtype == LH_BF16 ? launch_tree<bf16>(g, TL, dout, gpos, dog, G, st)
+                                        : launch_tree<float>(g, TL, dout, gpos, dog, G, st);
+        if (e != hipSuccess) return e;
         dim3 sg((unsigned)(g.S_pad / kRows), (unsigned)g.BH);
         if (dtype == LH_BF16)
             slot_dot_kernel<bf16><<<sg, kThreads, 0, st>>>((const bf16*)dog, og, lse, 1.f / scale, nd, nl, g.S, g.d);
         else
             slot_dot_kernel<float><<<sg, kThreads, 0, st>>>((const float*)dog, og, lse, 1.f / scale, nd, nl, g.S,
                                                             g.d);
-        hipError_t e = hipGetLastError();
+        e = hipGetLastError();
         if (e == hipSuccess && dogT) {   // f32 attention kernels take dOg transposed
             dim3 tg((unsigned)(g.S_pad / kRows), (unsigned)g.BH);
             transpose_kernel<float><<<tg, kThreads, tile_bytes<float>(g.d), st>>>((const float*)dog, (float*)dogT,

@@ -24,14 +24,15 @@ SMALL = [
     W("minimal_bf16", 1, 1, 16, 64, "bf16", 4, 3, 1, 107, False),    # N = p^(L-1), S = 9
     W("L2_bf16", 1, 2, 512, 64, "bf16", 4, 2, 40, 105, True),
     W("p2_L8_bf16", 1, 1, 2048, 64, "bf16", 2, 8, 5, 108, True),     # deepest pyramid
-    # p^(L-1) = 4096: whole f32 rows of a chunk's pyramid exceed the LDS, so the scatter
-    # backward takes its slot-centric form and pooling slices rows
+    # p^(L-1) = 4096: the coarse levels of a scatter-backward chunk exceed the LDS, so the
+    # scatter backward takes its slot-centric form and pooling slices rows
     W("p4_L7_bf16", 1, 1, 8192, 64, "bf16", 4, 7, 2, 109, True),
-    # large k against small coarse levels: the per-slot ranges would re-read dO ~3.5x, so the
-    # scatter backward takes its pyramid form (f32: with the transposed copy; p = 3, d = 128:
-    # a partial last chunk)
+    # large k against small coarse levels, pyramid form of the scatter backward (f32: with the
+    # transposed copy; p = 3, d = 128: a partial last chunk and idle lane groups)
     W("pyr_f32", 1, 2, 2048, 64, "f32", 4, 4, 256, 110, False),
     W("pyr_p3_d128_bf16", 1, 2, 1350, 128, "bf16", 3, 4, 200, 111, True),
+    # p = 5: the scatter backward takes its slot-centric form (f32: with the transposed copy)
+    W("p5_f32", 1, 2, 1250, 64, "f32", 5, 3, 9, 115, False),
     # p^(L-1) = 16384: no pass of the pooling chunk fits whole rows, so it takes passes of
     # p^2 tokens over rows sliced to 8 elements
     W("p4_L8_bf16", 1, 1, 16384, 64, "bf16", 4, 8, 3, 114, True),
