@@ -1,7 +1,9 @@
 // C ABI of the Lighthouse Attention library (declared in include/lighthouse.h):
 // host-side validation and sizing, then asynchronous launches on the caller's
-// stream.  No allocation, no synchronisation, no state beyond the constant
-// kernel table.
+// stream.  No allocation and no synchronisation.  State: the per-thread
+// measurement probe (lh_set_probe, lh_set_probe_flush), which the data path
+// only reads to record events, and the per-device address of the static
+// selection workspace of lh_score_topk_noalloc, looked up once under a lock.
 #include <math.h>
 #include <string.h>
 
