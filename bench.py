@@ -311,10 +311,30 @@ def attention_block(args, w, layer, o, dod, dq, dk, dv, timed):
                     "TFLOP/s count the GEMM flops only (the backward includes its transposes)"}
 
 
-def cpu_baseline(w, q, k, v, dout, nheads=6):
+def err_over_bound(got, ref, dtype):
+    """Worst error of `got` against `ref` as a fraction of the parity bound:
+    f32 max|a-b| / (1e-4 max|b|) over the tensor, bf16 max of
+    |a-b| / (2e-2 max(1, |b|)) element-wise (<= 1 passes)."""
+    import numpy as np
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    if not np.all(np.isfinite(got)):
+        return float("inf")
+    diff = np.abs(got - ref)
+    if dtype == "f32":
+        return float(diff.max() / (1e-4 * max(float(np.abs(ref).max()), 1e-30)))
+    return float((diff / (2e-2 * np.maximum(1.0, np.abs(ref)))).max())
+
+
+CPU_SAMPLE_HEADS = 6
+
+
+def cpu_baseline(w, q, k, v, dout, nheads=CPU_SAMPLE_HEADS, gpu=None):
     """The oracle as it stands on the first `nheads` heads of the workload:
     selection, pyramid, attention, scatter and the whole backward, per head;
-    scaled to the layer."""
+    scaled to the layer.  With `gpu` (the timed run's gidx, o, dq, dk, dv as
+    CPU tensors [B,H,...]) the same oracle results also give a parity verdict
+    for those heads: selection bit for bit, tensors against their bounds."""
     import numpy as np
     from oracle import lighthouse_oracle as orc
     try:
@@ -323,14 +343,20 @@ def cpu_baseline(w, q, k, v, dout, nheads=6):
     except Exception:
         cores = 1
     heads = w.B * w.H
-    nheads = min(nheads, heads)
+    nheads = min(nheads, w.H)
     dt = 0.0
+    sel_exact, worst = True, {}
     for h in range(nheads):
         qh, kh, vh, gh = (x[0, h].float().numpy().astype(np.float64) for x in (q, k, v, dout))
         t0 = time.perf_counter()
         st = orc.head_forward(qh, kh, vh, w.p, w.L, w.k, w.dtype)
-        orc.head_backward(st, gh)
+        bw = orc.head_backward(st, gh)
         dt += time.perf_counter() - t0
+        if gpu is not None:
+            sel_exact &= bool(np.array_equal(gpu["gidx"][0, h].numpy(), st["gidx"]))
+            for name, ref in (("o", st["O"]), ("dq", bw["dq"]), ("dk", bw["dk"]), ("dv", bw["dv"])):
+                e = err_over_bound(gpu[name][0, h].float().numpy(), ref, w.dtype)
+                worst[name] = max(worst.get(name, 0.0), e)
     per_head = dt / nheads
     cpu = "unknown"
     try:
@@ -341,7 +367,13 @@ def cpu_baseline(w, q, k, v, dout, nheads=6):
     return {"value": round(w.B * w.N / (per_head * heads), 1), "unit": "tokens/s", "cores": int(cores),
             "kind": "oracle", "cpu": cpu, "host_cpus": os.cpu_count(),
             "sample": f"{nheads} of {heads} heads (b=0, h<{nheads}), full fwd+bwd incl. selection, {dt:.1f} s "
-                      f"of CPU time; value = B*N / (mean time per head x {heads} heads)"}
+                      f"of CPU time; value = B*N / (mean time per head x {heads} heads)",
+            **({"parity": {"heads": nheads, "selection_bit_exact": sel_exact,
+                           "err_over_bound": {n: round(x, 4) for n, x in worst.items()},
+                           "pass": sel_exact and all(x <= 1.0 for x in worst.values()),
+                           "note": "the timed run's own outputs against the oracle on the sampled heads; "
+                                   "bound: bf16 |a-b| <= 2e-2 max(1,|b|), f32 max|a-b| <= 1e-4 max|b|"}}
+               if gpu is not None else {})}
 
 
 def median(xs):
@@ -352,9 +384,9 @@ def median(xs):
 def probe_kernels(lh, ev, step, names, reps, flush=None):
     """Median HIP-event duration of each kernel in `names` over `reps` probed
     steps (the probe records on the library's stream); with `flush` (a device
-    buffer of >= 512 MB) the library writes it just before every probed
+    buffer of >= 512 MB) the library reads it just before every probed
     launch, so the kernel starts with its inputs out of L2 and the Infinity
-    Cache."""
+    Cache (and with no dirty lines of its own to write back)."""
     import torch
     ids = {n: i for i, n in enumerate(KERNEL_NAMES)}
     if flush is not None:
@@ -589,7 +621,7 @@ def main():
     torch.cuda.synchronize()
 
     # every kernel's duration: median of a few probed steps, warm (inside running steps) and, for the
-    # bandwidth-bound ones, cold (the library writes a 1 GiB buffer just before the probed launch)
+    # bandwidth-bound ones, cold (the library reads a 1 GiB buffer just before the probed launch)
     ev = HipEvents()
     kernel_ms = probe_kernels(lh, ev, step, KERNEL_NAMES, args.probe_reps)
     flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -620,6 +652,13 @@ def main():
     dom_ms = sum(ev.elapsed_ms(s, e) for s, e in zip(starts, stops)) / args.steps
     step_ms = [a.elapsed_time(b) for a, b in step_ev]
     tokens_per_s = w.B * w.N * args.steps / elapsed
+    # the timed run's outputs of the heads the oracle samples, for its parity verdict (later
+    # measurements overwrite o, dq, dk, dv)
+    sampled = None
+    if not args.no_cpu_baseline:
+        nh = min(CPU_SAMPLE_HEADS, w.H)
+        sampled = {"gidx": layer.gidx[:1, :nh].cpu()}
+        sampled.update({n: t[:1, :nh].cpu() for n, t in (("o", o), ("dq", dq), ("dk", dk), ("dv", dv))})
 
     peaks = measured_peaks(dev)
     bound, work, unit = algorithmic_work(dominant, w, plan)
@@ -714,7 +753,7 @@ def main():
         torch.cuda.empty_cache()
         out["extreme_512k"] = extreme_512k(args, ev, peaks, dev)
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, q, k, v, dout)
+        out["cpu_baseline"] = cpu_baseline(w, q, k, v, dout, CPU_SAMPLE_HEADS, gpu=sampled)
         out["cpu_baseline"]["scaling"] = cpu_scaling(out["cpu_baseline"]["cores"])
     print(json.dumps(out), flush=True)
 

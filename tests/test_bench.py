@@ -71,3 +71,35 @@ def test_counter_summary_scales_by_the_copy(tmp_path, capsys):
     # 2.56 MB over 1 us: 2560 GB/s, 32.0% of the 8 TB/s peak
     assert "| pool_kernel | 2.6 | 1.0 | 2560 | 32.0% |" in out
     assert "- sources_sha256.select: `" in out
+
+
+def test_cpu_baseline_parity_verdict():
+    """The parity verdict of the oracle leg: outputs equal to the oracle's (as
+    stored in the dtype) pass; a changed slot or a perturbed gradient fails."""
+    import numpy as np
+    import torch
+    from long_context_pretraining_amd import inputs
+    from oracle import lighthouse_oracle as orc
+
+    w = inputs.Workload("bench_parity", 1, 2, 1024, 64, "bf16", 4, 3, 16, 21, True)
+    q, k, v = inputs.make_qkv(w)
+    dout = inputs.make_dout(w)
+    gidx, outs = [], {n: [] for n in ("o", "dq", "dk", "dv")}
+    for h in range(w.H):
+        f = lambda t: t[0, h].float().numpy().astype(np.float64)
+        st = orc.head_forward(f(q), f(k), f(v), w.p, w.L, w.k, w.dtype)
+        bw = orc.head_backward(st, f(dout))
+        gidx.append(torch.from_numpy(np.asarray(st["gidx"], np.int32)))
+        for n, x in (("o", st["O"]), ("dq", bw["dq"]), ("dk", bw["dk"]), ("dv", bw["dv"])):
+            outs[n].append(torch.from_numpy(x).to(torch.bfloat16))
+    gpu = {"gidx": torch.stack(gidx)[None]}
+    gpu.update({n: torch.stack(x)[None] for n, x in outs.items()})
+    r = bench.cpu_baseline(w, q, k, v, dout, nheads=2, gpu=gpu)["parity"]
+    assert r["pass"] and r["selection_bit_exact"] and r["heads"] == 2
+    assert max(r["err_over_bound"].values()) <= 0.5   # one bf16 rounding of the oracle's values
+    gpu["gidx"] = gpu["gidx"].clone()
+    gpu["gidx"][0, 1, 0] += 1
+    gpu["dk"] = gpu["dk"].clone()
+    gpu["dk"][0, 0, 5, 3] += 1.0
+    r = bench.cpu_baseline(w, q, k, v, dout, nheads=2, gpu=gpu)["parity"]
+    assert not r["pass"] and not r["selection_bit_exact"] and r["err_over_bound"]["dk"] > 1.0
