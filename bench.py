@@ -329,6 +329,36 @@ def err_over_bound(got, ref, dtype):
 CPU_SAMPLE_HEADS = 6
 
 
+def oracle_head(w, q, k, v, dout, h):
+    """The oracle's forward and backward of head (0, h), and its CPU time."""
+    import numpy as np
+    from oracle import lighthouse_oracle as orc
+    qh, kh, vh, gh = (x[0, h].float().numpy().astype(np.float64) for x in (q, k, v, dout))
+    t0 = time.perf_counter()
+    st = orc.head_forward(qh, kh, vh, w.p, w.L, w.k, w.dtype)
+    bw = orc.head_backward(st, gh)
+    return st, bw, time.perf_counter() - t0
+
+
+def head_parity(w, st, bw, gpu, h):
+    """Selection bit for bit and o, dq, dk, dv against their bounds, head (0, h)."""
+    import numpy as np
+    sel = bool(np.array_equal(gpu["gidx"][0, h].numpy(), st["gidx"]))
+    errs = {name: err_over_bound(gpu[name][0, h].float().numpy(), ref, w.dtype)
+            for name, ref in (("o", st["O"]), ("dq", bw["dq"]), ("dk", bw["dk"]), ("dv", bw["dv"]))}
+    return sel, errs
+
+
+def parity_512k(head):
+    """The oracle on head 0 of the 512K-token layer against the timed run's results."""
+    from long_context_pretraining_amd import inputs
+    w = inputs.WORKLOADS["extreme_512k"]
+    st, bw, secs = oracle_head(w, head["q"], head["k"], head["v"], head["dout"], 0)
+    sel, errs = head_parity(w, st, bw, head, 0)
+    return {"heads": 1, "selection_bit_exact": sel, "err_over_bound": {n: round(x, 4) for n, x in errs.items()},
+            "pass": sel and all(x <= 1.0 for x in errs.values()), "oracle_s": round(secs, 1)}
+
+
 def cpu_baseline(w, q, k, v, dout, nheads=CPU_SAMPLE_HEADS, gpu=None):
     """The oracle as it stands on the first `nheads` heads of the workload:
     selection, pyramid, attention, scatter and the whole backward, per head;
@@ -347,15 +377,12 @@ def cpu_baseline(w, q, k, v, dout, nheads=CPU_SAMPLE_HEADS, gpu=None):
     dt = 0.0
     sel_exact, worst = True, {}
     for h in range(nheads):
-        qh, kh, vh, gh = (x[0, h].float().numpy().astype(np.float64) for x in (q, k, v, dout))
-        t0 = time.perf_counter()
-        st = orc.head_forward(qh, kh, vh, w.p, w.L, w.k, w.dtype)
-        bw = orc.head_backward(st, gh)
-        dt += time.perf_counter() - t0
+        st, bw, secs = oracle_head(w, q, k, v, dout, h)
+        dt += secs
         if gpu is not None:
-            sel_exact &= bool(np.array_equal(gpu["gidx"][0, h].numpy(), st["gidx"]))
-            for name, ref in (("o", st["O"]), ("dq", bw["dq"]), ("dk", bw["dk"]), ("dv", bw["dv"])):
-                e = err_over_bound(gpu[name][0, h].float().numpy(), ref, w.dtype)
+            s_ok, errs = head_parity(w, st, bw, gpu, h)
+            sel_exact &= s_ok
+            for name, e in errs.items():
                 worst[name] = max(worst.get(name, 0.0), e)
     per_head = dt / nheads
     cpu = "unknown"
@@ -497,7 +524,7 @@ def timed_steps(step, n):
     return [a.elapsed_time(b) for a, b in evs]
 
 
-def extreme_512k(args, ev, peaks, dev):
+def extreme_512k(args, ev, peaks, dev, keep_head=False):
     """The 512K-token layer (B=1, H=16, N=524288, d=64, bf16, p=4, L=6,
     k=1536): step time, forward time, every kernel warm and cold, and one dense
     causal fwd+bwd step for the speedup.  Inputs are drawn on the device with
@@ -528,6 +555,12 @@ def extreme_512k(args, ev, peaks, dev):
     torch.cuda.synchronize()
     ts = timed_steps(step, args.extreme_steps)
     fwd = timed_steps(lambda: layer.forward(q, k, v, o), args.extreme_steps)
+    # head 0's inputs and the timed run's results for it, for the oracle leg's parity verdict
+    head = None
+    if keep_head:
+        head = {n: t[:1, :1].cpu() for n, t in (("q", q), ("k", k), ("v", v), ("dout", dout), ("o", o),
+                                                ("dq", dq), ("dk", dk), ("dv", dv))}
+        head["gidx"] = layer.gidx[:1, :1].cpu()
     flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
     kms = probe_kernels(lh, ev, step, KERNEL_NAMES, 3)
     kms_cold = probe_kernels(lh, ev, step, [n for n in KERNEL_NAMES if not n.startswith("attn")], 3, flush)
@@ -556,7 +589,7 @@ def extreme_512k(args, ev, peaks, dev):
         del dws, dwsb, lse
     del layer, q, k, v, dout, o, dq, dk, dv
     torch.cuda.empty_cache()
-    return out
+    return out, head
 
 
 def cpu_scaling(threads_all):
@@ -748,12 +781,15 @@ def main():
         "stages": stages,
         "attention_block": block,
     }
+    head_512k = None
     if headline and not args.no_extreme:
         del layer, qd, kd, vd, dod, o, dq, dk, dv, lse
         torch.cuda.empty_cache()
-        out["extreme_512k"] = extreme_512k(args, ev, peaks, dev)
+        out["extreme_512k"], head_512k = extreme_512k(args, ev, peaks, dev, keep_head=not args.no_cpu_baseline)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, q, k, v, dout, CPU_SAMPLE_HEADS, gpu=sampled)
+        if head_512k is not None:
+            out["cpu_baseline"]["parity_512k"] = parity_512k(head_512k)
         out["cpu_baseline"]["scaling"] = cpu_scaling(out["cpu_baseline"]["cores"])
     print(json.dumps(out), flush=True)
 
