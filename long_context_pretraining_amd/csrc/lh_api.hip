@@ -152,8 +152,9 @@ __global__ __launch_bounds__(256) void flush_kernel(const uint4* __restrict__ p,
 // Streams n16 16-byte words, 8 per thread per round (all loads issued before
 // any store) over a grid-stride of 16384 blocks: MODE 0 copies src to dst, 1
 // only reads src (an improbable, data-dependent store keeps the loads), 2 only
-// writes dst.  Loads are non-temporal and stores plain: on this GPU that pair
-// streamed fastest for buffers beyond the Infinity Cache.
+// writes dst.  Loads and stores are non-temporal: over 2 GiB (beyond the
+// Infinity Cache) non-temporal stores write ~8% faster than plain ones and
+// copy ~14% faster.
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 template <int MODE>
 __global__ __launch_bounds__(256) void hbm_kernel(u32x4_t* __restrict__ dst, const u32x4_t* __restrict__ src,
@@ -173,7 +174,7 @@ __global__ __launch_bounds__(256) void hbm_kernel(u32x4_t* __restrict__ dst, con
         for (int u = 0; u < U; ++u) {
             const size_t i = i0 + u * stride;
             if (MODE == 1) acc ^= v[u];
-            else if (i < n16) dst[i] = v[u];
+            else if (i < n16) __builtin_nontemporal_store(v[u], dst + i);
         }
     }
     if (MODE == 1 && acc.x == 0x9e3779b9u && acc.y == 0x7f4a7c15u && acc.z == 0x85ebca6bu && acc.w == 0xc2b2ae35u)
