@@ -510,21 +510,18 @@ __global__ __launch_bounds__(1024) void scatter_bwd_tree_kernel(const T* __restr
         const int32_t v = gp[idx];
         sv[j] = ok ? v : -1;
     }
-    const int units = C / U, per = nthr / NVEC;
-    const int vv = tid % NVEC;
-    int u = tid / NVEC;
+    // lane group u (the launch has at least C / U groups) owns rows u U .. u U + U - 1
+    const int units = C / U;
+    const int vv = tid % NVEC, u = tid / NVEC;
     VT x[U];
-    auto load_unit = [&](int uu) {
 #pragma unroll
-        for (int j = 0; j < U; ++j) {
-            const int64_t tp = c0 + (int64_t)uu * U + j;
-            const bool ok = uu < units && tp >= 1 && tp <= G.N;
-            const int64_t row = ok ? tp - 1 : 0;
-            const VT v = __builtin_nontemporal_load(reinterpret_cast<const VT*>(dh + row * D + vv * VEC));
-            x[j] = ok ? v : VT{};
-        }
-    };
-    load_unit(u);
+    for (int j = 0; j < U; ++j) {
+        const int64_t tp = c0 + (int64_t)u * U + j;
+        const bool ok = u < units && tp >= 1 && tp <= G.N;
+        const int64_t row = ok ? tp - 1 : 0;
+        const VT v = __builtin_nontemporal_load(reinterpret_cast<const VT*>(dh + row * D + vv * VEC));
+        x[j] = ok ? v : VT{};
+    }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int i = tid + j * nthr;
@@ -532,8 +529,7 @@ __global__ __launch_bounds__(1024) void scatter_bwd_tree_kernel(const T* __restr
         else if (i < C + n1) s1l[i - C] = sv[j];
     }
     __syncthreads();
-    for (; u < units; u += per) {
-        if (u != tid / NVEC) load_unit(u);
+    if (u < units) {
         float a2[VEC];
 #pragma unroll
         for (int e = 0; e < VEC; ++e) a2[e] = 0.f;
@@ -744,9 +740,10 @@ hipError_t launch_scatter_fwd(const LhGeom& g, int dtype, const float* og, const
 namespace {
 constexpr int kTreeLds = 48 * 1024;
 
-// Block shape of the pyramid form: one pass of 256 threads where the chunk
-// allows (each NVEC-lane group on p^2 rows), the chunk rounded up to a
-// multiple of p^(L-1); chunk = 0 when p, d or the LDS rule it out.
+// Block shape of the pyramid form: one lane group of NVEC lanes per p^2 rows
+// of the chunk, 256 threads where p^(L-1) allows, otherwise the chunk rounded
+// up to a multiple of p^(L-1) and up to 1024 threads; chunk = 0 (slot-centric
+// form) when p, d, that thread count or the LDS rule it out.
 struct TreeLaunch {
     TreeP P;
     int threads;
@@ -759,10 +756,11 @@ TreeLaunch tree_plan(const LhGeom& g, int dtype) {
     const int64_t m = g.pw[g.L - 1] > U ? g.pw[g.L - 1] : U;
     int64_t C = (256 / nvec) * U;
     C = (C + m - 1) / m * m;
-    int64_t threads = C / U * nvec;
-    threads = threads > 1024 ? 1024 : (threads + 63) / 64 * 64;
+    int64_t threads = C / U * nvec;   // one lane group per p^2 rows, all in one pass
+    if (threads > 1024) return t;
+    threads = (threads + 63) / 64 * 64;
     const int64_t n1 = C / g.p;
-    if (C + n1 > 4 * threads || C > (1 << 20)) return t;   // the kernel stages the slots in four loads per thread
+    if (C + n1 > 4 * threads) return t;   // the kernel stages the slots in four loads per thread
     const int64_t s1_off = C, rows_off = ((C + n1) * 4 + 15) & ~(int64_t)15;
     int64_t rows = 0;
     for (int l = 2; l + 1 < g.L; ++l) rows += C / g.pw[l];
