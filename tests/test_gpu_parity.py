@@ -33,6 +33,10 @@ SMALL = [
     W("pyr_p3_d128_bf16", 1, 2, 1350, 128, "bf16", 3, 4, 200, 111, True),
     # p = 5: the scatter backward takes its slot-centric form (f32: with the transposed copy)
     W("p5_f32", 1, 2, 1250, 64, "f32", 5, 3, 9, 115, False),
+    # pyramid form of the scatter backward with level 1 as the top (p = 3, f32, a partial last
+    # chunk) and with levels 3 and 4 from LDS at d = 128 over two batches
+    W("tree_p3_L2_f32", 1, 2, 999, 64, "f32", 3, 2, 50, 116, False),
+    W("tree_p2_L5_d128_bf16", 2, 2, 2048, 128, "bf16", 2, 5, 37, 117, True),
     # p^(L-1) = 16384: no pass of the pooling chunk fits whole rows, so it takes passes of
     # p^2 tokens over rows sliced to 8 elements
     W("p4_L8_bf16", 1, 1, 16384, 64, "bf16", 4, 8, 3, 114, True),
