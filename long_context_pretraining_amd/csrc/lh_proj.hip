@@ -165,20 +165,37 @@ template <> __device__ __forceinline__ void store8<float>(float* dst, const floa
 // C[M x Nc] = A[M x K] B[Nc x K]^T over the k-blocks of this block's split
 // (blockIdx.z); f32 accumulation, one rounding to OutT.  Blocks are numbered
 // so that each XCD (blocks are dealt to the 8 XCDs in turn) works on a
-// contiguous range of C tiles, row tile by row tile: tiles that share rows of
-// A then share that XCD's L2.
+// contiguous range of C tiles.  With group_m > 0 (unsplit products whose row
+// tiles divide into whole groups per XCD) the range is walked in groups of
+// group_m row tiles, column by column: the ~32 blocks an XCD runs at once then
+// cover group_m row tiles of A and a few column tiles of B, instead of ~3 row
+// tiles and every column tile of B (W, 6 MB at d_model = 1024, more than the
+// XCD's 4 MB L2).  Otherwise row tile by row tile.
 template <class OpA, class OpB, class Epi, typename OutT>
 __global__ __launch_bounds__(kGThreads, 1) void gemm_nt_kernel(OpA A, OpB B, Epi E, int64_t M, int64_t Nc,
                                                                int nkb, int kb_per_split, int tiles_n,
-                                                               int tiles) {
+                                                               int tiles, int group_m) {
     extern __shared__ __align__(16) unsigned char smem[];
     const int lane = threadIdx.x & 63, wave = wave_id();
     const int col = lane & 31, h = lane >> 5;
     const int wm = wave / kWN, wn = wave % kWN;
-    const int per_xcd = (tiles + 7) / 8;
-    const int tile = (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8);
-    if (tile >= tiles) return;   // uniform per block
-    const int64_t m0 = (int64_t)(tile / tiles_n) * kBM, n0 = (int64_t)(tile % tiles_n) * kBN;
+    int mt, nt;
+    if (group_m > 0) {
+        // each XCD takes tiles_m / 8 consecutive row tiles; inside, groups of group_m row
+        // tiles are walked column-major, so the blocks running together share both operands
+        const int tiles_m = tiles / tiles_n, rows_per_xcd = tiles_m / 8;
+        const int xcd = (int)(blockIdx.x % 8), li = (int)(blockIdx.x / 8);
+        const int g = li / (group_m * tiles_n), r = li - g * group_m * tiles_n;
+        mt = xcd * rows_per_xcd + g * group_m + r % group_m;
+        nt = r / group_m;
+    } else {
+        const int per_xcd = (tiles + 7) / 8;
+        const int tile = (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8);
+        if (tile >= tiles) return;   // uniform per block
+        mt = tile / tiles_n;
+        nt = tile % tiles_n;
+    }
+    const int64_t m0 = (int64_t)mt * kBM, n0 = (int64_t)nt * kBN;
     const int kb0 = blockIdx.z * kb_per_split;
     const int kb1 = kb0 + kb_per_split < nkb ? kb0 + kb_per_split : nkb;
 
@@ -348,8 +365,11 @@ hipError_t gemm_nt(const OpA& A, const OpB& B, const Epi& E, int64_t M, int64_t 
     static const hipError_t attr =
         hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, kGemmLds);
     (void)attr;
+    const int tiles_m = tiles / tiles_n;
+    const int group_m = (splits == 1 && tiles_m % 64 == 0) ? 8 : 0;   // whole groups of 8 row tiles per XCD
+    // (a split-k product has too few row tiles to spread over the XCDs this way)
     dim3 grid((unsigned)((tiles + 7) / 8 * 8), 1, (unsigned)splits);
-    kern<<<grid, kGThreads, kGemmLds, st>>>(A, B, E, M, Nc, nkb, per, tiles_n, tiles);
+    kern<<<grid, kGThreads, kGemmLds, st>>>(A, B, E, M, Nc, nkb, per, tiles_n, tiles, group_m);
     return hipGetLastError();
 }
 
