@@ -28,6 +28,9 @@ constexpr int kThreads = 256;
 // the scatter backward it was slower, so those keep ordinary loads).
 template <class V>
 __device__ __forceinline__ V load_stream(const V* p) { return __builtin_nontemporal_load(p); }
+// The pooled levels are stored non-temporally as well: left in the caches as
+// dirty lines, they were written back during the next kernels (at 512K tokens
+// the score pass ran 35 -> 25 us and the gather 78 -> 56 us without them).
 
 // One lane's chunk of CW elements (as CW / VEC 16-byte vectors): squares
 // rounded to f32 and added left to right.
@@ -173,7 +176,7 @@ __global__ __launch_bounds__(kThreads) void pool_kernel(const T* __restrict__ x0
 #pragma unroll
                     for (int i = 0; i < VEC; ++i) dst[i] = acc[j][i];
                 }
-                *reinterpret_cast<VT*>(ph + (P.offu[1] + (int64_t)cidx * P.epc[1] + e1 + e) * P.d + dim0 + vv * VEC) = out;
+                __builtin_nontemporal_store(out, reinterpret_cast<VT*>(ph + (P.offu[1] + (int64_t)cidx * P.epc[1] + e1 + e) * P.d + dim0 + vv * VEC));
             }
         }
         if (P.norms && blockIdx.z < 2) {
@@ -214,7 +217,7 @@ __global__ __launch_bounds__(kThreads) void pool_kernel(const T* __restrict__ x0
 #pragma unroll
                 for (int i = 0; i < VEC; ++i) dst[i] = acc[i];
             }
-            *reinterpret_cast<VT*>(ph + (P.offu[2] + (int64_t)cidx * P.epc[2] + e2 + e) * P.d + dim0 + vv * VEC) = out;
+            __builtin_nontemporal_store(out, reinterpret_cast<VT*>(ph + (P.offu[2] + (int64_t)cidx * P.epc[2] + e2 + e) * P.d + dim0 + vv * VEC));
         }
         __syncthreads();   // the scratch region is reused by the next pass
     }
@@ -243,7 +246,7 @@ __global__ __launch_bounds__(kThreads) void pool_kernel(const T* __restrict__ x0
 #pragma unroll
                 for (int i = 0; i < VEC; ++i) dst[i] = acc[i];
             }
-            *reinterpret_cast<VT*>(ph + (P.offu[l] + (int64_t)cidx * P.epc[l] + e) * P.d + dim0 + vv * VEC) = out;
+            __builtin_nontemporal_store(out, reinterpret_cast<VT*>(ph + (P.offu[l] + (int64_t)cidx * P.epc[l] + e) * P.d + dim0 + vv * VEC));
         }
         __syncthreads();
         prev_off = cur_off;
